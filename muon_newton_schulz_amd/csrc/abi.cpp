@@ -1,0 +1,568 @@
+// C ABI of the Muon / Newton-Schulz step: argument validation, workspace planning and the
+// drivers that sequence the kernels of one step on the caller's stream.
+//
+// Method: page "Dion3: Full-stack orthogonal updates" -- Eq. (1) (Muon), Eq. (2) (NorMuon),
+// section "Standard Newton-Schulz", Theorem 2 and the restart of Algorithm 3 (Gram NS),
+// Algorithm 4 (Dion3 row selection), section "4. Megabatched Communication" (matrices of
+// one shape are processed as one batch).
+#include "muon_ns.h"
+#include "mns_internal.h"
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+using namespace mns;
+
+namespace {
+
+constexpr int64_t kMaxDim = 65536;
+constexpr int64_t kMaxElems = 2147483647LL;
+constexpr int kMaxT = 64;
+constexpr int kChunk = kMaxPack;      // matrices per batched launch sequence
+
+// Carves 256-byte aligned slices from the workspace; with a null base it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+// Geometry of the Newton-Schulz problem for a rows x cols matrix: it runs on the short
+// side (n <= m), a tall matrix through its transpose, in a zero-padded n_p x m_p iterate
+// whose entries are stored times S (a power of two chosen so the float16 iterate keeps
+// its entries well inside the normal range: X_0 entries ~ S/sqrt(nm), later ~ S/sqrt(m)).
+struct Geo {
+  int64_t rows, cols, n, m, n_p, m_p;
+  bool tall;
+  Elem elem;
+  float S;
+};
+
+Geo make_geo(int64_t rows, int64_t cols, Store st) {
+  Geo g;
+  g.rows = rows;
+  g.cols = cols;
+  g.tall = rows > cols;
+  g.n = g.tall ? cols : rows;
+  g.m = g.tall ? rows : cols;
+  g.n_p = pad_up(g.n);
+  g.m_p = pad_up(g.m);
+  g.elem = st == Store::BF16 ? Elem::F16 : Elem::F32;
+  if (g.elem == Elem::F16) {
+    int e = (int)std::lround(0.5 * std::log2((double)g.m));
+    if (e < 0) e = 0;
+    if (e > 12) e = 12;
+    g.S = std::ldexp(1.0f, e);
+  } else {
+    g.S = 1.0f;
+  }
+  return g;
+}
+
+struct NsBuffers {
+  void* X0 = nullptr;
+  void* X1 = nullptr;
+  void* sq[6] = {};        // n_p x n_p scratch: standard uses 2, Gram uses 6
+  int64_t x_stride = 0, sq_stride = 0;
+};
+
+void carve_ns(Carver& cv, const Geo& g, int count, int kind, NsBuffers& b) {
+  const size_t es = (size_t)elem_bytes(g.elem);
+  b.x_stride = g.n_p * g.m_p;
+  b.sq_stride = g.n_p * g.n_p;
+  b.X0 = cv.take<char>(es * count * b.x_stride);
+  b.X1 = cv.take<char>(es * count * b.x_stride);
+  const int nsq = kind == MNS_NS_GRAM ? 6 : 2;
+  for (int i = 0; i < nsq; ++i) b.sq[i] = cv.take<char>(es * count * b.sq_stride);
+}
+
+#define MNS_HIP(expr)                               \
+  do {                                              \
+    if ((expr) != hipSuccess) return MNS_ERR_HIP;   \
+  } while (0)
+
+GemmDesc sym_desc(const Geo& g, int count, const NsBuffers& b, const void* A, const void* B,
+                  int64_t ldab, int64_t sab, int K, void* C) {
+  GemmDesc d;
+  d.elem = g.elem;
+  d.A = A; d.lda = ldab; d.sA = sab;
+  d.B = B; d.ldb = ldab; d.sB = sab; d.b_kmajor = true;
+  d.C = C; d.ldc = g.n_p; d.sC = b.sq_stride;
+  d.M = (int)g.n_p; d.N = (int)g.n_p; d.K = K; d.batch = count;
+  d.sym = true;
+  return d;
+}
+
+// C (n_p x m_p) = alpha * L X + beta * D, L: n_p x n_p, X: n_p x m_p (n-contiguous operand).
+GemmDesc left_desc(const Geo& g, int count, const NsBuffers& b, const void* L, const void* X,
+                   void* C) {
+  GemmDesc d;
+  d.elem = g.elem;
+  d.A = L; d.lda = g.n_p; d.sA = b.sq_stride;
+  d.B = X; d.ldb = g.m_p; d.sB = b.x_stride; d.b_kmajor = false;
+  d.C = C; d.ldc = g.m_p; d.sC = b.x_stride;
+  d.M = (int)g.n_p; d.N = (int)g.m_p; d.K = (int)g.n_p; d.batch = count;
+  return d;
+}
+
+// Standard quintic NS on the normalised iterate in b.X0 (section "Standard Newton-Schulz"):
+// A = X X^T, B = b A + c A^2, X <- a X + B X. Returns the buffer holding X_T.
+mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, const float* abc,
+                        hipStream_t s, void** out) {
+  void* xin = b.X0;
+  void* xout = b.X1;
+  void* A = b.sq[0];
+  void* B = b.sq[1];
+  const float inv_s2 = 1.0f / (g.S * g.S);
+  for (int t = 0; t < T; ++t) {
+    const float a = abc[3 * t], bb = abc[3 * t + 1], c = abc[3 * t + 2];
+    GemmDesc gram = sym_desc(g, count, b, xin, xin, g.m_p, b.x_stride, (int)g.m_p, A);
+    gram.alpha = inv_s2;
+    MNS_HIP(gemm(gram, s));
+    const void* L = A;
+    float lalpha = bb;
+    if (c != 0.0f) {
+      GemmDesc poly = sym_desc(g, count, b, A, A, g.n_p, b.sq_stride, (int)g.n_p, B);
+      poly.alpha = c;
+      poly.beta = bb;
+      poly.D = A; poly.ldd = g.n_p; poly.sD = b.sq_stride;
+      MNS_HIP(gemm(poly, s));
+      L = B;
+      lalpha = 1.0f;
+    }
+    GemmDesc upd = left_desc(g, count, b, L, xin, xout);
+    upd.alpha = lalpha;
+    upd.beta = a;
+    upd.D = xin; upd.ldd = g.m_p; upd.sD = b.x_stride;
+    MNS_HIP(gemm(upd, s));
+    void* tmp = xin; xin = xout; xout = tmp;
+  }
+  *out = xin;
+  return MNS_OK;
+}
+
+// Gram Newton-Schulz (Theorem 2) with restarts (Algorithm 3): R = X X^T; per iteration
+// Z = a I + b R + c R^2, R <- R Z^2 (skipped when unused), Q <- Q Z (Q_1 = Z_1);
+// a restart before t forms X <- Q X, R <- X X^T, Q <- I. Output Q X.
+mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const float* abc,
+                    uint32_t restart_mask, hipStream_t s, void** out) {
+  void* xcur = b.X0;
+  void* xoth = b.X1;
+  void* R = b.sq[0];
+  void* Rt = b.sq[1];
+  void* Z = b.sq[2];
+  void* Z2 = b.sq[3];
+  void* Q = b.sq[4];
+  void* Qt = b.sq[5];
+  const float inv_s2 = 1.0f / (g.S * g.S);
+  const int n = (int)g.n_p;
+
+  GemmDesc gram = sym_desc(g, count, b, xcur, xcur, g.m_p, b.x_stride, (int)g.m_p, R);
+  gram.alpha = inv_s2;
+  MNS_HIP(gemm(gram, s));
+  bool q_identity = true;
+  for (int t = 1; t <= T; ++t) {
+    const float a = abc[3 * (t - 1)], bb = abc[3 * (t - 1) + 1], c = abc[3 * (t - 1) + 2];
+    if (t > 1 && ((restart_mask >> t) & 1u)) {
+      if (!q_identity) {
+        MNS_HIP(gemm(left_desc(g, count, b, Q, xcur, xoth), s));
+        void* tmp = xcur; xcur = xoth; xoth = tmp;
+      }
+      GemmDesc re = sym_desc(g, count, b, xcur, xcur, g.m_p, b.x_stride, (int)g.m_p, R);
+      re.alpha = inv_s2;
+      MNS_HIP(gemm(re, s));
+      q_identity = true;
+    }
+    GemmDesc zd = sym_desc(g, count, b, R, R, g.n_p, b.sq_stride, n, Z);
+    zd.alpha = c;
+    zd.beta = bb;
+    zd.D = R; zd.ldd = g.n_p; zd.sD = b.sq_stride;
+    zd.gamma = a;
+    zd.diag_limit = (int)g.n;
+    MNS_HIP(gemm(zd, s));
+    if (t < T && !((restart_mask >> (t + 1)) & 1u)) {
+      MNS_HIP(gemm(sym_desc(g, count, b, Z, Z, g.n_p, b.sq_stride, n, Z2), s));
+      MNS_HIP(gemm(sym_desc(g, count, b, R, Z2, g.n_p, b.sq_stride, n, Rt), s));
+      void* tmp = R; R = Rt; Rt = tmp;
+    }
+    if (q_identity) {
+      void* tmp = Q; Q = Z; Z = tmp;
+      q_identity = false;
+    } else {
+      MNS_HIP(gemm(sym_desc(g, count, b, Q, Z, g.n_p, b.sq_stride, n, Qt), s));
+      void* tmp = Q; Q = Qt; Qt = tmp;
+    }
+  }
+  if (q_identity) {
+    *out = xcur;
+  } else {
+    MNS_HIP(gemm(left_desc(g, count, b, Q, xcur, xoth), s));
+    *out = xoth;
+  }
+  return MNS_OK;
+}
+
+mns_status run_ns(const Geo& g, int count, const NsBuffers& b, int kind, int T, const float* abc,
+                  uint32_t restart_mask, hipStream_t s, void** out) {
+  if (kind == MNS_NS_GRAM) return run_gram(g, count, b, T, abc, restart_mask, s, out);
+  return run_standard(g, count, b, T, abc, s, out);
+}
+
+// ---- validation helpers --------------------------------------------------------------------
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+mns_status check_shape(int64_t batch, int64_t rows, int64_t cols) {
+  if (batch < 1 || rows < 1 || cols < 1) return MNS_ERR_SHAPE;
+  if (rows > kMaxDim || cols > kMaxDim || rows * cols > kMaxElems) return MNS_ERR_SHAPE;
+  if (batch > kMaxElems / (rows * cols)) return MNS_ERR_SHAPE;
+  return MNS_OK;
+}
+
+mns_status check_dtype(int dt) {
+  return (dt == MNS_F32 || dt == MNS_BF16) ? MNS_OK : MNS_ERR_DTYPE;
+}
+
+mns_status check_ns(int T, const float* abc, int kind, uint32_t restart_mask) {
+  if (T < 1 || T > kMaxT) return MNS_ERR_PARAM;
+  if (!abc) return MNS_ERR_NULL;
+  for (int i = 0; i < 3 * T; ++i)
+    if (!std::isfinite(abc[i])) return MNS_ERR_PARAM;
+  if (kind != MNS_NS_STANDARD && kind != MNS_NS_GRAM) return MNS_ERR_PARAM;
+  if (kind == MNS_NS_STANDARD && restart_mask != 0) return MNS_ERR_PARAM;
+  // valid restart bits: 2..T
+  const uint64_t allowed = ((T >= 31 ? 0xFFFFFFFFull : ((1ull << (T + 1)) - 1))) & ~3ull;
+  if ((uint64_t)restart_mask & ~allowed) return MNS_ERR_PARAM;
+  return MNS_OK;
+}
+
+mns_status check_ws(void* ws, size_t have, size_t need) {
+  if (!ws) return MNS_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MNS_ERR_WORKSPACE;
+  if (have < need) return MNS_ERR_WORKSPACE;
+  return MNS_OK;
+}
+
+int64_t k_rows(double f, int64_t rows) {
+  int64_t k = (int64_t)std::ceil(f * (double)rows);
+  if (k < 1) k = 1;
+  if (k > rows) k = rows;
+  return k;
+}
+
+// Shape groups: matrices of equal (rows, cols), in order of first appearance.
+struct Group {
+  int64_t rows, cols;
+  std::vector<int> idx;
+};
+
+std::vector<Group> group_by_shape(const mns_matrix* mats, int count) {
+  std::vector<Group> gs;
+  for (int i = 0; i < count; ++i) {
+    bool found = false;
+    for (auto& g : gs)
+      if (g.rows == mats[i].rows && g.cols == mats[i].cols) {
+        g.idx.push_back(i);
+        found = true;
+        break;
+      }
+    if (!found) gs.push_back(Group{mats[i].rows, mats[i].cols, {i}});
+  }
+  return gs;
+}
+
+mns_status validate_step(const mns_matrix* mats, int count, const mns_hparams* hp,
+                         bool need_ptrs) {
+  if (!mats || !hp) return MNS_ERR_NULL;
+  if (count < 1) return MNS_ERR_SHAPE;
+  mns_status st = check_dtype(hp->dtype);
+  if (st != MNS_OK) return st;
+  st = check_ns(hp->T, hp->abc, hp->kind, hp->restart_mask);
+  if (st != MNS_OK) return st;
+  if (!std::isfinite(hp->mu) || !std::isfinite(hp->lr)) return MNS_ERR_PARAM;
+  if (!(hp->row_fraction > 0.0 && hp->row_fraction <= 1.0)) return MNS_ERR_PARAM;
+  if (hp->normuon != 0 && hp->normuon != 1) return MNS_ERR_PARAM;
+  if (hp->normuon && (!(hp->beta2 >= 0.f && hp->beta2 <= 1.f) || !(hp->eps >= 0.f) ||
+                      !std::isfinite(hp->eps)))
+    return MNS_ERR_PARAM;
+  for (int i = 0; i < count; ++i) {
+    st = check_shape(1, mats[i].rows, mats[i].cols);
+    if (st != MNS_OK) return st;
+    if (need_ptrs) {
+      if (!mats[i].W || !mats[i].M || !mats[i].G) return MNS_ERR_NULL;
+      if (hp->normuon && !mats[i].v) return MNS_ERR_NULL;
+      if (!aligned(mats[i].W, 16) || !aligned(mats[i].M, 16) || !aligned(mats[i].G, 16) ||
+          (mats[i].v && !aligned(mats[i].v, 4)))
+        return MNS_ERR_PARAM;
+    }
+  }
+  return MNS_OK;
+}
+
+// Workspace layout of one chunk (<= kChunk matrices of one shape) of muon_step.
+struct StepWs {
+  float* partials = nullptr;
+  float* xscale = nullptr;
+  NsBuffers ns;
+  float* part = nullptr;
+  float* rowscale = nullptr;
+  float* l1 = nullptr;
+  int32_t* S = nullptr;
+  float* Msel = nullptr;
+  int nblk = 0, chunks = 0;
+};
+
+size_t carve_step(void* base, const Geo& g, int count, int64_t rows, int64_t cols, bool dion,
+                  int64_t k, int kind, StepWs& w) {
+  Carver cv(base);
+  w.nblk = dion ? (int)k : norm_blocks(rows * cols);
+  w.partials = cv.take<float>((size_t)count * w.nblk);
+  w.xscale = cv.take<float>((size_t)count);
+  carve_ns(cv, g, count, kind, w.ns);
+  const int64_t stored_rows = g.tall ? g.m : g.n;     // rows of the matrix NS ran on
+  w.chunks = (int)((g.tall ? g.n_p : g.m_p) / kPad);
+  w.part = cv.take<float>((size_t)count * w.chunks * stored_rows);
+  w.rowscale = cv.take<float>((size_t)count * stored_rows);
+  if (dion) {
+    w.l1 = cv.take<float>((size_t)count * rows);
+    w.S = cv.take<int32_t>((size_t)count * k);
+    w.Msel = cv.take<float>((size_t)count * k * cols);
+  }
+  return cv.off + 256;
+}
+
+size_t step_bytes(const mns_matrix* mats, int count, const mns_hparams* hp) {
+  const Store st = hp->dtype == MNS_BF16 ? Store::BF16 : Store::F32;
+  const bool dion = hp->row_fraction < 1.0;
+  size_t need = 0;
+  for (const Group& gr : group_by_shape(mats, count)) {
+    const int c = (int)gr.idx.size() < kChunk ? (int)gr.idx.size() : kChunk;
+    const int64_t k = dion ? k_rows(hp->row_fraction, gr.rows) : gr.rows;
+    const Geo g = make_geo(k, gr.cols, st);
+    StepWs w;
+    const size_t b = carve_step(nullptr, g, c, gr.rows, gr.cols, dion, k, hp->kind, w);
+    if (b > need) need = b;
+  }
+  return need;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mns_status_string(int status) {
+  switch (status) {
+    case MNS_OK: return "MNS_OK";
+    case MNS_ERR_NULL: return "MNS_ERR_NULL: a required pointer is NULL";
+    case MNS_ERR_SHAPE: return "MNS_ERR_SHAPE: a size is out of range";
+    case MNS_ERR_DTYPE: return "MNS_ERR_DTYPE: unknown storage dtype";
+    case MNS_ERR_PARAM: return "MNS_ERR_PARAM: invalid hyperparameter or alignment";
+    case MNS_ERR_WORKSPACE: return "MNS_ERR_WORKSPACE: workspace NULL, misaligned or too small";
+    case MNS_ERR_HIP: return "MNS_ERR_HIP: a HIP launch failed";
+    default: return "unknown mns_status";
+  }
+}
+
+int mns_version(void) { return 100; }
+
+mns_status mns_step_workspace_size(const mns_matrix* mats, int count, const mns_hparams* hp,
+                                   size_t* bytes) {
+  if (!bytes) return MNS_ERR_NULL;
+  const mns_status st = validate_step(mats, count, hp, false);
+  if (st != MNS_OK) return st;
+  *bytes = step_bytes(mats, count, hp);
+  return MNS_OK;
+}
+
+mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  mns_status st = validate_step(mats, count, hp, true);
+  if (st != MNS_OK) return st;
+  st = check_ws(workspace, workspace_bytes, step_bytes(mats, count, hp));
+  if (st != MNS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Store sto = hp->dtype == MNS_BF16 ? Store::BF16 : Store::F32;
+  const bool dion = hp->row_fraction < 1.0;
+
+  for (const Group& gr : group_by_shape(mats, count)) {
+    const int64_t rows = gr.rows, cols = gr.cols;
+    const int64_t k = dion ? k_rows(hp->row_fraction, rows) : rows;
+    const Geo g = make_geo(k, cols, sto);      // the matrix NS runs on: k x cols
+    for (size_t c0 = 0; c0 < gr.idx.size(); c0 += kChunk) {
+      const int c = (int)((gr.idx.size() - c0) < (size_t)kChunk ? gr.idx.size() - c0 : kChunk);
+      PtrPack Wp = {}, Mp = {}, Gp = {}, Vp = {};
+      for (int i = 0; i < c; ++i) {
+        const mns_matrix& mm = mats[gr.idx[c0 + i]];
+        Wp.p[i] = mm.W;
+        Mp.p[i] = mm.M;
+        Gp.p[i] = const_cast<void*>(mm.G);
+        Vp.p[i] = mm.v;
+      }
+      StepWs w;
+      carve_step(workspace, g, c, rows, cols, dion, k, hp->kind, w);
+
+      if (!dion) {
+        MNS_HIP(momentum(Mp, Gp, sto, c, rows * cols, hp->mu, w.partials, s));
+        MNS_HIP(finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s));
+        MNS_HIP(normalize(&Mp, nullptr, true, sto, c, rows, cols, g.tall, w.xscale, g.elem,
+                          w.ns.X0, g.n_p, g.m_p, s));
+      } else {
+        MNS_HIP(momentum_l1(Mp, Gp, sto, c, rows, cols, w.l1, s));
+        MNS_HIP(topk_rows(w.l1, c, rows, k, w.S, s));
+        MNS_HIP(gather_decay(Mp, c, cols, k, w.S, hp->mu, w.Msel, w.partials, s));
+        MNS_HIP(finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s));
+        MNS_HIP(normalize(nullptr, w.Msel, true, sto, c, k, cols, g.tall, w.xscale, g.elem,
+                          w.ns.X0, g.n_p, g.m_p, s));
+      }
+      void* O = nullptr;
+      st = run_ns(g, c, w.ns, hp->kind, hp->T, hp->abc, hp->restart_mask, s, &O);
+      if (st != MNS_OK) return st;
+      const float inv_s = 1.0f / g.S;
+      if (hp->normuon) {
+        MNS_HIP(row_sumsq_x(O, g.elem, g.n_p, g.m_p, c, g.n, g.m, g.tall, w.part, s));
+        MNS_HIP(normuon_finalize(w.part, w.chunks, c, k, cols, &Vp, nullptr, 0,
+                                 dion ? w.S : nullptr, hp->beta2, hp->eps, inv_s * inv_s, inv_s,
+                                 w.rowscale, s));
+      } else {
+        MNS_HIP(fill(w.rowscale, (int64_t)c * k, inv_s, s));
+      }
+      MNS_HIP(weight_update(Wp, sto, c, k, cols, O, g.elem, g.n_p, g.m_p, g.tall, w.rowscale,
+                            dion ? w.S : nullptr, k, hp->lr, s));
+    }
+  }
+  return MNS_OK;
+}
+
+// ---- standalone orthogonalisation ------------------------------------------------------------
+
+static size_t ns_bytes(const Geo& g, int c, int kind, int64_t rows, int64_t cols,
+                       NsBuffers* b, float** partials, float** xscale, void* base) {
+  Carver cv(base);
+  NsBuffers tmp;
+  NsBuffers& nb = b ? *b : tmp;
+  float* p = cv.take<float>((size_t)c * norm_blocks(rows * cols));
+  float* x = cv.take<float>((size_t)c);
+  carve_ns(cv, g, c, kind, nb);
+  if (partials) *partials = p;
+  if (xscale) *xscale = x;
+  return cv.off + 256;
+}
+
+mns_status mns_ns_workspace_size(int dtype, int64_t batch, int64_t rows, int64_t cols, int kind,
+                                 size_t* bytes) {
+  if (!bytes) return MNS_ERR_NULL;
+  mns_status st = check_dtype(dtype);
+  if (st != MNS_OK) return st;
+  st = check_shape(batch, rows, cols);
+  if (st != MNS_OK) return st;
+  if (kind != MNS_NS_STANDARD && kind != MNS_NS_GRAM) return MNS_ERR_PARAM;
+  const Geo g = make_geo(rows, cols, dtype == MNS_BF16 ? Store::BF16 : Store::F32);
+  const int c = batch < kChunk ? (int)batch : kChunk;
+  *bytes = ns_bytes(g, c, kind, rows, cols, nullptr, nullptr, nullptr, nullptr);
+  return MNS_OK;
+}
+
+static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch, int64_t rows,
+                                int64_t cols, int T, const float* abc, int kind,
+                                uint32_t restart_mask, void* ws, size_t ws_bytes, void* stream) {
+  mns_status st = check_dtype(dtype);
+  if (st != MNS_OK) return st;
+  st = check_shape(batch, rows, cols);
+  if (st != MNS_OK) return st;
+  if (!X || !O) return MNS_ERR_NULL;
+  st = check_ns(T, abc, kind, restart_mask);
+  if (st != MNS_OK) return st;
+  if (!aligned(X, 16) || !aligned(O, 16)) return MNS_ERR_PARAM;
+  const Store sto = dtype == MNS_BF16 ? Store::BF16 : Store::F32;
+  const Geo g = make_geo(rows, cols, sto);
+  const int cmax = batch < kChunk ? (int)batch : kChunk;
+  st = check_ws(ws, ws_bytes, ns_bytes(g, cmax, kind, rows, cols, nullptr, nullptr, nullptr, nullptr));
+  if (st != MNS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esz = sto == Store::BF16 ? 2 : 4;
+  for (int64_t b0 = 0; b0 < batch; b0 += kChunk) {
+    const int c = (int)((batch - b0) < kChunk ? batch - b0 : kChunk);
+    NsBuffers nb;
+    float *partials = nullptr, *xscale = nullptr;
+    ns_bytes(g, c, kind, rows, cols, &nb, &partials, &xscale, ws);
+    const char* xin = static_cast<const char*>(X) + (size_t)b0 * rows * cols * esz;
+    char* out = static_cast<char*>(O) + (size_t)b0 * rows * cols * esz;
+    MNS_HIP(sumsq(xin, sto, c, rows * cols, partials, s));
+    MNS_HIP(finalize_scale(partials, norm_blocks(rows * cols), c, g.S, xscale, s));
+    MNS_HIP(normalize(nullptr, xin, false, sto, c, rows, cols, g.tall, xscale, g.elem, nb.X0,
+                      g.n_p, g.m_p, s));
+    void* res = nullptr;
+    st = run_ns(g, c, nb, kind, T, abc, restart_mask, s, &res);
+    if (st != MNS_OK) return st;
+    MNS_HIP(export_output(res, g.elem, g.n_p, g.m_p, c, rows, cols, g.tall, 1.0f / g.S, out, sto, s));
+  }
+  return MNS_OK;
+}
+
+mns_status ns_orthogonalize(const void* X, void* O, int dtype, int64_t batch, int64_t rows,
+                            int64_t cols, int T, const float* abc, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return orthogonalize(X, O, dtype, batch, rows, cols, T, abc, MNS_NS_STANDARD, 0u, workspace,
+                       workspace_bytes, stream);
+}
+
+mns_status gram_ns_orthogonalize(const void* X, void* O, int dtype, int64_t batch, int64_t rows,
+                                 int64_t cols, int T, const float* abc, uint32_t restart_mask,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return orthogonalize(X, O, dtype, batch, rows, cols, T, abc, MNS_NS_GRAM, restart_mask,
+                       workspace, workspace_bytes, stream);
+}
+
+// ---- standalone NorMuon ------------------------------------------------------------------------
+
+static size_t normuon_bytes(int64_t batch, int64_t rows, float** part, float** rowscale,
+                            void* base) {
+  Carver cv(base);
+  float* p = cv.take<float>((size_t)batch * rows);
+  float* r = cv.take<float>((size_t)batch * rows);
+  if (part) *part = p;
+  if (rowscale) *rowscale = r;
+  return cv.off + 256;
+}
+
+mns_status mns_normuon_workspace_size(int64_t batch, int64_t rows, int64_t cols, size_t* bytes) {
+  if (!bytes) return MNS_ERR_NULL;
+  const mns_status st = check_shape(batch, rows, cols);
+  if (st != MNS_OK) return st;
+  *bytes = normuon_bytes(batch, rows, nullptr, nullptr, nullptr);
+  return MNS_OK;
+}
+
+mns_status normuon_scale(void* O, int dtype, int64_t batch, int64_t rows, int64_t cols, float* v,
+                         float beta2, float eps, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  mns_status st = check_dtype(dtype);
+  if (st != MNS_OK) return st;
+  st = check_shape(batch, rows, cols);
+  if (st != MNS_OK) return st;
+  if (!O || !v) return MNS_ERR_NULL;
+  if (!(beta2 >= 0.f && beta2 <= 1.f) || !(eps >= 0.f) || !std::isfinite(eps)) return MNS_ERR_PARAM;
+  if (!aligned(O, 16) || !aligned(v, 4)) return MNS_ERR_PARAM;
+  if (batch > 65535) return MNS_ERR_SHAPE;
+  st = check_ws(workspace, workspace_bytes, normuon_bytes(batch, rows, nullptr, nullptr, nullptr));
+  if (st != MNS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Store sto = dtype == MNS_BF16 ? Store::BF16 : Store::F32;
+  float *part = nullptr, *rowscale = nullptr;
+  normuon_bytes(batch, rows, &part, &rowscale, workspace);
+  MNS_HIP(row_sumsq_stored(O, sto, (int)batch, rows, cols, part, s));
+  MNS_HIP(normuon_finalize(part, 1, (int)batch, rows, cols, nullptr, v, rows, nullptr, beta2, eps,
+                           1.0f, 1.0f, rowscale, s));
+  MNS_HIP(rowscale_apply(O, sto, (int)batch, rows, cols, rowscale, s));
+  return MNS_OK;
+}
+
+}  // extern "C"

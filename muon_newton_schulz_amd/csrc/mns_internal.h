@@ -1,0 +1,132 @@
+// Internal declarations shared by the library's translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mns {
+
+// Type of the Newton-Schulz iterate and of the Gram-side matrices on the device.
+// bfloat16 storage runs the iteration in float16 with float32 accumulation (the stabilised
+// Gram NS casts in float16; a bfloat16 iterate loses too much precision); float32 storage
+// runs it in float32 end to end.
+enum class Elem { F16 = 0, F32 = 1 };
+
+// Storage type of caller buffers (W, G, X, O).
+enum class Store { F32 = 0, BF16 = 1 };
+
+inline int elem_bytes(Elem e) { return e == Elem::F16 ? 2 : 4; }
+
+// Caller pointers of up to kMaxPack same-shape matrices, passed by value as a kernel
+// argument (no device-side pointer table, nothing to upload).
+constexpr int kMaxPack = 16;
+struct PtrPack {
+  void* p[kMaxPack];
+};
+
+// Every NS-side matrix in the workspace is zero-padded to multiples of this size, so the
+// GEMM kernels run on whole tiles with no bounds checks; zero padding is invariant under
+// every product and polynomial the iterations form.
+constexpr int kPad = 256;
+inline int64_t pad_up(int64_t x) { return (x + kPad - 1) / kPad * kPad; }
+
+// ---------------------------------------------------------------------------------------
+// GEMM (gemm.hip): C = alpha * op(A, B) + beta * D + gamma * I
+//   A: M x K, k-contiguous rows (lda).  B: N x K k-contiguous (b_kmajor) or K x N
+//   n-contiguous.  C, D: M x N row-major.  Batched over blockIdx.z with element strides.
+//   sym: M == N, the result is known to be symmetric; only tiles on or above the diagonal
+//   are computed and each is also stored mirrored (within a diagonal tile the upper
+//   triangle is mirrored), so C is exactly symmetric.
+//   M, N, K must be multiples of kPad.
+// ---------------------------------------------------------------------------------------
+struct GemmDesc {
+  Elem elem = Elem::F16;
+  const void* A = nullptr; int64_t lda = 0, sA = 0;
+  const void* B = nullptr; int64_t ldb = 0, sB = 0; bool b_kmajor = true;
+  void* C = nullptr; int64_t ldc = 0, sC = 0;
+  const void* D = nullptr; int64_t ldd = 0, sD = 0;
+  int M = 0, N = 0, K = 0, batch = 1;
+  float alpha = 1.f, beta = 0.f, gamma = 0.f;
+  int diag_limit = 0;          // gamma is added at (i, i) for i < diag_limit
+  bool sym = false;
+};
+hipError_t gemm(const GemmDesc& d, hipStream_t s);
+
+// ---------------------------------------------------------------------------------------
+// Elementwise / reduction kernels (elementwise.hip). All are deterministic: fixed
+// reduction orders, no floating-point atomics.
+// ---------------------------------------------------------------------------------------
+
+// Blocks of the momentum / sum-of-squares kernels for a matrix of `elems` elements.
+int norm_blocks(int64_t elems);
+
+// M <- mu M + G over `count` same-size matrices; partials[b * nblk + blk] = partial sum of
+// the new M^2.
+hipError_t momentum(const PtrPack& M, const PtrPack& G, Store g_store, int count,
+                    int64_t elems, float mu, float* partials, hipStream_t s);
+
+// partials of sum X^2 for X of storage type `st` (X_b = X + b * elems).
+hipError_t sumsq(const void* X, Store st, int count, int64_t elems, float* partials,
+                 hipStream_t s);
+
+// xscale[b] = S / sqrt(sum_blk partials[b * nblk + blk]), 0 for a zero matrix.
+hipError_t finalize_scale(const float* partials, int nblk, int count, float S, float* xscale,
+                          hipStream_t s);
+
+// X0 (n_p x m_p, Elem) = xscale * src, zero padded; src is rows x cols (float32 when
+// src_f32, else storage `st`); tall (rows > cols) is written transposed.
+// src pointers: a pack (per matrix) or, when pack == nullptr, base + b * rows * cols.
+hipError_t normalize(const PtrPack* pack, const void* base, bool src_f32, Store st, int count,
+                     int64_t rows, int64_t cols, bool tall, const float* xscale, Elem e,
+                     void* X0, int64_t n_p, int64_t m_p, hipStream_t s);
+
+// O (rows x cols, storage st) = inv_s * X (Elem, n_p x m_p layout, transposed if tall).
+hipError_t export_output(const void* X, Elem e, int64_t n_p, int64_t m_p, int count,
+                         int64_t rows, int64_t cols, bool tall, float inv_s, void* O, Store st,
+                         hipStream_t s);
+
+// Per stored row, partial sums of O^2 over 256-wide chunks of the row:
+//   part[b][chunk][row] for the X-layout iterate (n_p x m_p); stored rows are X rows
+//   (wide) or X columns (tall).
+hipError_t row_sumsq_x(const void* X, Elem e, int64_t n_p, int64_t m_p, int count,
+                       int64_t n, int64_t m, bool tall, float* part, hipStream_t s);
+
+// Same for a caller matrix O (rows x cols, storage st): part[b][chunk][row].
+hipError_t row_sumsq_stored(const void* O, Store st, int count, int64_t rows, int64_t cols,
+                            float* part, hipStream_t s);
+
+// NorMuon (Eq. 2) per matrix: r_i = inv_s2 * sum_chunk part; v <- beta2 v + (1-beta2) r/cols;
+// d_i = 1/(sqrt(v)+eps); ratio = sqrt(sum r / sum r d^2); rowscale_i = ratio d_i out_scale.
+// rowidx (nullable): v index of row i. v pointers per matrix in the pack (or v_base +
+// b * v_stride when pack is null).
+hipError_t normuon_finalize(const float* part, int chunks, int count, int64_t rows,
+                            int64_t cols, const PtrPack* v_pack, float* v_base,
+                            int64_t v_stride, const int32_t* rowidx, float beta2, float eps,
+                            float inv_s2, float out_scale, float* rowscale, hipStream_t s);
+
+// rowscale[b][i] = value (plain Muon: every row scaled alike).
+hipError_t fill(float* p, int64_t n, float value, hipStream_t s);
+
+// W[rowidx[i]][j] -= lr * rowscale[i] * O[i][j]  (O from the X-layout iterate, transposed
+// when tall; rowidx null = identity).
+hipError_t weight_update(const PtrPack& W, Store st, int count, int64_t rows, int64_t cols,
+                         const void* X, Elem e, int64_t n_p, int64_t m_p, bool tall,
+                         const float* rowscale, const int32_t* rowidx, int64_t rowidx_stride,
+                         float lr, hipStream_t s);
+
+// O[b][i][j] *= rowscale[b][i] in place (storage st).
+hipError_t rowscale_apply(void* O, Store st, int count, int64_t rows, int64_t cols,
+                          const float* rowscale, hipStream_t s);
+
+// Dion3 (Algorithm 4): M <- M + G with per-row l1 norms of the new M.
+hipError_t momentum_l1(const PtrPack& M, const PtrPack& G, Store g_store, int count,
+                       int64_t rows, int64_t cols, float* l1, hipStream_t s);
+// S[b][rank] = row for the k rows of largest l1 (ties: lower index first).
+hipError_t topk_rows(const float* l1, int count, int64_t rows, int64_t k, int32_t* S,
+                     hipStream_t s);
+// Msel[b][p][:] = M[S[p]][:]; M[S[p]][:] *= mu; partials[b][p] = sum Msel[p][:]^2.
+hipError_t gather_decay(const PtrPack& M, int count, int64_t cols, int64_t k,
+                        const int32_t* S, float mu, float* Msel, float* partials,
+                        hipStream_t s);
+
+}  // namespace mns

@@ -1,0 +1,58 @@
+"""Test-side helpers: moving stored bits between NumPy and torch, and the comparison rules.
+
+Tolerances (relative Frobenius error per matrix, after each step): 1e-4 when W, G, X are
+float32 and 2e-2 when they are bfloat16.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def to_device(stored: np.ndarray, storage: str, device="cuda") -> torch.Tensor:
+    if storage == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(stored).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(stored, dtype=np.float32)).to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> exact float64 values (bfloat16 widened by the oracle's decoder)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return oracle.bf16_bits_to_f64(t.view(torch.int16).numpy().view(np.uint16))
+    return t.numpy().astype(np.float64)
+
+
+def stored_f64(stored: np.ndarray, storage: str) -> np.ndarray:
+    if storage == "bf16":
+        return oracle.bf16_bits_to_f64(stored)
+    return np.asarray(stored, dtype=np.float64)
+
+
+def rel(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
+
+
+def ulp_half(w: np.ndarray, storage: str) -> np.ndarray:
+    """Half the spacing of the storage format at |w| (the bound of one rounding)."""
+    w = np.abs(np.asarray(w, dtype=np.float64))
+    mant_bits = 8 if storage == "bf16" else 24
+    e = np.floor(np.log2(np.maximum(w, 2.0 ** -126)))
+    return 0.5 * 2.0 ** (e - (mant_bits - 1))
+
+
+def check_weight(W_gpu, W0, delta_ref, storage: str, what: str = "W") -> float:
+    """W_gpu = round(W0 + delta_gpu) with ||delta_gpu - delta_ref|| <= tol ||delta_ref||, so
+    ||W_gpu - W0 - delta_ref|| <= tol ||delta_ref|| + ||ulp/2|| (one rounding per element)."""
+    W_gpu = np.asarray(W_gpu, dtype=np.float64)
+    err = np.linalg.norm(W_gpu - W0 - delta_ref)
+    bound = TOL[storage] * np.linalg.norm(delta_ref) + np.linalg.norm(ulp_half(W0 + delta_ref, storage))
+    assert err <= bound, f"{what}: |W - W0 - delta| = {err:.4g} > bound {bound:.4g}"
+    return float(err / max(np.linalg.norm(delta_ref), 1e-300))

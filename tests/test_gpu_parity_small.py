@@ -1,0 +1,196 @@
+"""GPU parity at sizes the oracle finishes in seconds: several 256 x 256 tiles plus ragged
+tails, tall and wide, batched, every entry point through the C ABI, against the fp64
+oracle. Tolerances: relative Frobenius 2e-2 (bfloat16 storage), 1e-4 (float32)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import muon_newton_schulz_amd as mns
+import synthetic
+from helpers import TOL, check_weight, rel, stored_f64, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _inputs(shape, storage, seed, batch=1, dist="normal"):
+    xs = [synthetic.gradient(dist, *shape, storage, 900, seed, i) for i in range(batch)]
+    return np.stack(xs)
+
+
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(300, 700), (700, 300), (256, 512), (1, 9), (37, 37)])
+@pytest.mark.parametrize("coeff", [(1.0, 0.0, 0.0), (0.0, 1.0, 0.0), (0.0, 0.0, 1.0), (0.5, -0.3, 0.2)])
+def test_ns_single_polynomial(storage, shape, coeff):
+    """One NS step with one monomial at a time isolates X/||X||, the Gram product X X^T,
+    the symmetric product A^2 and the rectangular B X."""
+    _say("case", storage, shape, coeff)
+    x = _inputs(shape, storage, 1, batch=2)
+    X = to_device(x, storage)
+    O = mns.ns_orthogonalize(X, [coeff])
+    torch.cuda.synchronize()
+    got = to_f64(O)
+    for b in range(2):
+        want = oracle.newton_schulz(stored_f64(x[b], storage), [coeff])
+        assert rel(got[b], want) < TOL[storage], (b, rel(got[b], want))
+
+
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(300, 700), (700, 300), (512, 1024), (520, 520)])
+def test_ns_quintic(storage, shape):
+    _say("case", storage, shape)
+    x = _inputs(shape, storage, 2, batch=3, dist="student_t")
+    O = mns.ns_orthogonalize(to_device(x, storage), [QUINTIC] * 5)
+    torch.cuda.synchronize()
+    got = to_f64(O)
+    for b in range(3):
+        want = oracle.newton_schulz(stored_f64(x[b], storage), [QUINTIC] * 5)
+        assert rel(got[b], want) < TOL[storage]
+
+
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(300, 900), (900, 300), (512, 512)])
+@pytest.mark.parametrize("restarts", [(), (3,), (2, 4)])
+def test_gram_ns(storage, shape, restarts):
+    _say("case", storage, shape, restarts)
+    x = _inputs(shape, storage, 3, batch=2)
+    O = mns.gram_ns_orthogonalize(to_device(x, storage), [QUINTIC] * 5, restart_before=restarts)
+    torch.cuda.synchronize()
+    got = to_f64(O)
+    for b in range(2):
+        want = oracle.gram_newton_schulz(stored_f64(x[b], storage), [QUINTIC] * 5, restarts)
+        assert rel(got[b], want) < TOL[storage]
+
+
+def test_zero_matrix_gives_zero_and_keeps_weights():
+    _say("case zero")
+    X = torch.zeros(64, 300, dtype=torch.bfloat16, device="cuda")
+    assert not mns.ns_orthogonalize(X, [QUINTIC] * 5).any()
+    assert not mns.gram_ns_orthogonalize(X, [QUINTIC] * 5).any()
+    W = torch.randn(64, 300, device="cuda").to(torch.bfloat16)
+    W0 = W.clone()
+    M = torch.zeros(64, 300, device="cuda")
+    v = torch.zeros(64, device="cuda")
+    mns.muon_step(W, M, X, v, mu=0.9, lr=0.1, coeffs=[QUINTIC] * 5, normuon=True)
+    torch.cuda.synchronize()
+    assert torch.equal(W, W0) and not M.any() and not v.any()
+
+
+def _step_case(shapes, storage, kind, restarts, normuon, f, seed, steps=1, w_zero=False):
+    mu, lr = 0.9, 0.05
+    Ws = [synthetic.weight(r, c, storage, 950, i, zero=w_zero) for i, (r, c) in enumerate(shapes)]
+    Ms = [synthetic.state(r, c, 950, i, scale=0.5) for i, (r, c) in enumerate(shapes)]
+    vs = [np.abs(synthetic.state(r, 1, 951, i, scale=0.01)).reshape(r) for i, (r, c) in enumerate(shapes)]
+    W = [to_device(w, storage) for w in Ws]
+    M = [torch.from_numpy(m).cuda() for m in Ms]
+    v = [torch.from_numpy(x.astype(np.float32)).cuda() for x in vs]
+    for step in range(steps):
+        Gs = [synthetic.gradient("student_t", r, c, storage, 952, step + seed, i)
+              for i, (r, c) in enumerate(shapes)]
+        W_before = [to_f64(t) for t in W]
+        M_before = [to_f64(t) for t in M]
+        v_before = [to_f64(t) for t in v]
+        mns.muon_step(W, M, [to_device(g, storage) for g in Gs], v if normuon else None, mu=mu,
+                      lr=lr, coeffs=[QUINTIC] * 5, kind=kind, restart_before=restarts,
+                      normuon=normuon, beta2=0.9, eps=1e-8, row_fraction=f)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            g64 = stored_f64(Gs[i], storage)
+            if f < 1.0:
+                ref = oracle.dion3_step(W_before[i], M_before[i], g64, mu=mu, lr=lr, f=f,
+                                        coeffs=[QUINTIC] * 5, kind=kind, restart_before=restarts,
+                                        normuon=normuon, v=v_before[i], beta2=0.9, eps=1e-8,
+                                        storage=storage)
+            else:
+                ref = oracle.muon_step(W_before[i], M_before[i], g64, mu=mu, lr=lr,
+                                       coeffs=[QUINTIC] * 5, kind=kind, restart_before=restarts,
+                                       normuon=normuon, v=v_before[i], beta2=0.9, eps=1e-8,
+                                       storage=storage)
+            check_weight(to_f64(W[i]), W_before[i], ref["W_exact"] - W_before[i], storage,
+                         f"W[{i}] step {step}")
+            assert rel(to_f64(M[i]), ref["M"]) < 1e-6, f"M[{i}]"
+            if normuon:
+                assert rel(to_f64(v[i]), ref["v"]) < TOL[storage], f"v[{i}]"
+
+
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+@pytest.mark.parametrize("normuon", [False, True])
+def test_muon_step_mixed_shapes(storage, normuon):
+    """Several shapes in one call: grouping by shape, tall and wide, ragged sizes."""
+    _say("case", storage, normuon)
+    shapes = [(300, 700), (300, 700), (700, 300), (256, 256), (300, 700)]
+    _step_case(shapes, storage, "standard", (), normuon, 1.0, 0, steps=2)
+
+
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+def test_muon_step_gram_kind(storage):
+    _say("case", storage)
+    _step_case([(260, 1100), (1100, 260)], storage, "gram", (3,), True, 1.0, 10)
+
+
+def test_muon_step_many_matrices_one_shape():
+    """More matrices of one shape than one batched launch holds (chunking)."""
+    _say("case 20 x 128x384")
+    _step_case([(128, 384)] * 20, "bf16", "standard", (), True, 1.0, 20, w_zero=True)
+
+
+@pytest.mark.parametrize("shape,f", [((64, 200), 0.25), ((200, 64), 0.5), ((100, 300), 1.0 / 3)])
+def test_dion3_step(shape, f):
+    _say("case dion3", shape, f)
+    _step_case([shape, shape], "bf16", "gram", (3,), True, f, 30, steps=3)
+
+
+def test_dion3_selection_matches_oracle():
+    """Top-k rows by l1 with ties to the lower index: exact indices (the ties here are exact
+    in float32: duplicated rows)."""
+    _say("case dion3 ties")
+    rows, cols = 44, 96
+    rng = np.random.default_rng(5)
+    base = rng.standard_normal((rows // 2, cols)).astype(np.float32)
+    G = np.concatenate([base, base[::-1]], axis=0)           # every l1 norm appears twice
+    # k = ceil(44 / 4) = 11 splits one tied pair: its lower-index row must win
+    W = torch.zeros(rows, cols, device="cuda")
+    M = torch.zeros(rows, cols, device="cuda")
+    mns.muon_step(W, M, torch.from_numpy(G).cuda(), mu=0.5, lr=0.1, coeffs=[QUINTIC] * 5,
+                  kind="gram", restart_before=(3,), row_fraction=0.25)
+    torch.cuda.synchronize()
+    S = oracle.select_rows(G.astype(np.float64), 11)
+    decayed = np.where(np.isclose(M.cpu().numpy(), 0.5 * G).all(axis=1) & ~np.isclose(G, 0).all(axis=1))[0]
+    assert sorted(decayed.tolist()) == sorted(S.tolist())
+    moved = np.where(W.cpu().numpy().any(axis=1))[0]
+    assert sorted(moved.tolist()) == sorted(S.tolist())
+
+
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+def test_normuon_scale(storage):
+    _say("case normuon", storage)
+    rng = np.random.default_rng(6)
+    o = (rng.standard_normal((3, 70, 130)) * rng.uniform(0.2, 2.0, (3, 70, 1))).astype(np.float32)
+    stored = synthetic.encode(o, storage)
+    v0 = rng.uniform(0, 0.1, (3, 70)).astype(np.float32)
+    O = to_device(stored, storage)
+    v = torch.from_numpy(v0.copy()).cuda()
+    mns.normuon_scale(O, v, beta2=0.9, eps=1e-6)
+    torch.cuda.synchronize()
+    got, gv = to_f64(O), to_f64(v)
+    for b in range(3):
+        vn, u = oracle.normuon_update(stored_f64(stored[b], storage), v0[b].astype(np.float64), 0.9, 1e-6)
+        assert rel(got[b], u) < TOL[storage] * 0.5
+        assert rel(gv[b], vn) < 1e-5
+
+
+def test_repeat_runs_are_bitwise_identical():
+    _say("case determinism")
+    x = _inputs((520, 1400), "bf16", 7, batch=2)
+    X = to_device(x, "bf16")
+    a = mns.ns_orthogonalize(X, [QUINTIC] * 5)
+    b = mns.ns_orthogonalize(X, [QUINTIC] * 5)
+    c = mns.gram_ns_orthogonalize(X, [QUINTIC] * 5)
+    d = mns.gram_ns_orthogonalize(X, [QUINTIC] * 5)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(c, d)
