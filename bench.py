@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the Muon / Newton-Schulz optimizer step on one MI355X.
+
+A step is one muon_step call over a workload's matrices (momentum, normalisation, T
+Newton-Schulz iterations, NorMuon and the weight update), inputs resident in HBM.
+Prints one JSON line: NS algorithmic TFLOP/s over the whole step, step ms, the dominant
+kernel's roofline (from hipEvents the library records around its launches during the timed
+steps), a per-kernel breakdown, and the fp64 oracle timed on a bounded sample on the host.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {1..5}] [--kind standard|gram]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense MFMA and HBM3E)
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--kind", choices=["standard", "gram"], default=None,
+                    help="override the workload's Newton-Schulz variant")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-clock budget of the oracle sample")
+    return ap.parse_args()
+
+
+def build_inputs(wl, torch, np, synthetic, dev):
+    import numpy
+    W, M, G, V = [], [], [], []
+    for idx, rows, cols in wl.matrices():
+        g = synthetic.gradient(wl.dist, rows, cols, wl.storage, wl.index, 0, idx)
+        if wl.storage == "bf16":
+            G.append(torch.from_numpy(g.view(numpy.int16)).view(torch.bfloat16).to(dev))
+            W.append(torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev))
+        else:
+            G.append(torch.from_numpy(g).to(dev))
+            W.append(torch.zeros(rows, cols, dtype=torch.float32, device=dev))
+        M.append(torch.zeros(rows, cols, dtype=torch.float32, device=dev))
+        V.append(torch.zeros(rows, dtype=torch.float32, device=dev))
+    return W, M, G, V
+
+
+def cpu_baseline(wl, kind, budget_s):
+    """The fp64 oracle as it stands, timed on a bounded sample of the workload: the
+    Newton-Schulz orthogonalisation of the workload's first matrix (first iteration only when
+    all T would overrun the budget). Returns the oracle's algorithmic TFLOP/s (the same FLOP
+    accounting as the GPU value)."""
+    import numpy as np
+    import oracle
+    import synthetic
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    idx, rows, cols = wl.matrices()[0]
+    if wl.row_fraction < 1.0:
+        rows = oracle.rows_for_fraction(wl.row_fraction, rows)
+    g = synthetic.gradient(wl.dist, rows, cols, wl.storage, wl.index, 0, idx)
+    x = synthetic.decode(g, wl.storage).astype(np.float64)
+    coeffs = wl.coeff_table()
+    restarts = (wl.restart_before or (3,)) if kind == "gram" else ()
+
+    def run(cs):
+        c = oracle.FlopCounter()
+        t0 = time.perf_counter()
+        oracle.orthogonalize(x, cs, kind, restarts if len(cs) == len(coeffs) else (), c)
+        return c.algorithmic, time.perf_counter() - t0
+
+    flops, dt = run(coeffs[:1])
+    used = 1
+    if dt * len(coeffs) < budget_s and len(coeffs) > 1:
+        flops, dt = run(coeffs)
+        used = len(coeffs)
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{kind} NS of matrix 0 ({rows}x{cols}) of {wl.n_matrices}, {used} of "
+                      f"{len(coeffs)} iterations, fp64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this optimizer-step library has no multi-GPU "
+              "path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import muon_newton_schulz_amd as mns
+    import synthetic
+
+    wl = synthetic.CONFIGS[args.config]
+    kind = args.kind or wl.kind
+    restarts = wl.restart_before if kind == "gram" else ()
+    if kind == "gram" and not restarts:
+        restarts = (3,)
+    dev = torch.device("cuda:0")
+    W, M, G, V = build_inputs(wl, torch, np, synthetic, dev)
+    kw = dict(mu=wl.mu, lr=wl.lr, coeffs=wl.coeff_table(), kind=kind, restart_before=restarts,
+              normuon=wl.normuon, beta2=wl.beta2, eps=wl.eps, row_fraction=wl.row_fraction)
+    v_arg = V if wl.normuon else None
+    ws = torch.empty(mns.step_workspace_size(W, M, G, v_arg, **kw), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mns.muon_step(W, M, G, v_arg, workspace=ws, stream=stream, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mns.profile_begin()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stats = mns.profile_end()
+    total_ms = e0.elapsed_time(e1)
+    ms_step = total_ms / args.steps
+
+    gemm = [s for s in stats if s["flops"] > 0]
+    ns_flops = sum(s["flops"] for s in gemm) / args.steps
+    ns_ms = sum(s["ms"] for s in gemm) / args.steps
+    dtype = "f32" if wl.storage == "f32" else "f16"
+    peak = PEAK_TFLOPS[dtype]
+    value = ns_flops / (ms_step * 1e-3) / 1e12
+
+    kernels = {}
+    for s in stats:
+        avg_us = 1e3 * s["ms"] / max(s["launches"], 1)
+        ent = {"launches": s["launches"], "avg_us": round(avg_us, 2),
+               "share": round(s["ms"] / max(total_ms, 1e-9), 4)}
+        if s["flops"] > 0:
+            tf = s["flops"] / (s["ms"] * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), frac=round(tf / peak, 4))
+        else:
+            gbs = s["bytes"] / (s["ms"] * 1e-3) / 1e9
+            ent.update(gbs=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[s["name"]] = ent
+
+    dom = max(stats, key=lambda s: s["ms"])
+    if dom["flops"] > 0:
+        ach = dom["flops"] / dom["launches"] / (dom["ms"] / dom["launches"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom["name"], "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+    else:
+        ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom["name"], "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, kind, args.cpu_seconds)
+
+    out = {
+        "metric": "NS orthogonalization TFLOP/s + Muon step ms per shape; % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if wl.storage == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "ns": kind, "T": wl.T, "normuon": wl.normuon,
+                   "row_fraction": wl.row_fraction, "matrices": wl.n_matrices,
+                   "storage": wl.storage},
+        "ns_gemm_ms_per_step": round(ns_ms, 4),
+        "ns_gemm_tflops": round(ns_flops / (ns_ms * 1e-3) / 1e12, 1) if ns_ms > 0 else None,
+        "ns_flops_per_step": ns_flops,
+        "mfma_frac_step": round(value / peak, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

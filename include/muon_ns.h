@@ -19,8 +19,9 @@
  *     Momentum M and NorMuon state v are always float32.
  *   - Ownership: the caller owns every buffer, including the workspace, whose size the
  *     matching *_workspace_size call returns. The library allocates no device memory,
- *     keeps no state between calls and is reentrant; calls on different streams must
- *     use different workspaces.
+ *     keeps no state between calls (apart from an open profiling session, see the end of
+ *     this file) and is reentrant; calls on different streams must use different
+ *     workspaces.
  *   - Errors: arguments are validated synchronously, before anything is enqueued, and
  *     reported as an mns_status; nothing is enqueued when a call returns an error other
  *     than MNS_ERR_HIP. MNS_ERR_HIP means a kernel launch failed (the stream may hold
@@ -152,6 +153,29 @@ mns_status mns_normuon_workspace_size(int64_t batch, int64_t rows, int64_t cols,
 mns_status normuon_scale(void* O, int dtype, int64_t batch, int64_t rows, int64_t cols,
                          float* v, float beta2, float eps, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* ---- Instrumentation ---------------------------------------------------------------------
+ * Between mns_profile_begin() and mns_profile_end() every kernel launch the library makes is
+ * bracketed by a pair of hipEvents recorded on the launch's stream. mns_profile_end() waits
+ * for those events and writes one entry per kernel (in order of first launch): the launch
+ * count, the summed event time in milliseconds and the summed algorithmic work of those
+ * launches -- FLOPs for the GEMMs (a symmetric product counted at half the dense 2MNK, as the
+ * page prices a symmetric GEMM) and HBM bytes for the elementwise and reduction kernels.
+ * Process-global, not thread-safe; meant for benchmarks. Costs one event pair per launch.
+ *   out      (host) array of `capacity` entries; entries beyond `capacity` are dropped
+ *   count    (host) out: number of distinct kernels seen
+ * mns_profile_end returns MNS_ERR_PARAM when no session is open, MNS_ERR_HIP when an event
+ * could not be created or read. */
+typedef struct mns_kernel_stat {
+  char name[64];
+  int64_t launches;
+  double ms;
+  double flops;
+  double bytes;
+} mns_kernel_stat;
+
+mns_status mns_profile_begin(void);
+mns_status mns_profile_end(mns_kernel_stat* out, int capacity, int* count);
 
 #ifdef __cplusplus
 }

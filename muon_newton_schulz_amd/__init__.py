@@ -18,7 +18,7 @@ from ._abi import (MNS_BF16, MNS_F32, MNS_NS_GRAM, MNS_NS_STANDARD, MnsError,  #
 
 __all__ = ["muon_step", "ns_orthogonalize", "gram_ns_orthogonalize", "normuon_scale",
            "step_workspace_size", "ns_workspace_size", "normuon_workspace_size",
-           "restart_mask", "MnsError", "load"]
+           "restart_mask", "profile_begin", "profile_end", "MnsError", "load"]
 
 _KINDS = {"standard": MNS_NS_STANDARD, "gram": MNS_NS_GRAM}
 
@@ -201,3 +201,19 @@ def normuon_scale(O: torch.Tensor, v: torch.Tensor, beta2: float = 0.95, eps: fl
                             ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)),
           "normuon_scale")
     return O
+
+
+def profile_begin() -> None:
+    """Start bracketing every library kernel launch with hipEvents (see mns_profile_begin)."""
+    check(load().mns_profile_begin(), "mns_profile_begin")
+
+
+def profile_end() -> list[dict]:
+    """Close the session; per kernel: launches, event ms, algorithmic FLOPs and bytes."""
+    lib = load()
+    cap = 64
+    arr = (_abi.MnsKernelStat * cap)()
+    n = ctypes.c_int(0)
+    check(lib.mns_profile_end(arr, cap, ctypes.byref(n)), "mns_profile_end")
+    return [{"name": arr[i].name.decode(), "launches": arr[i].launches, "ms": arr[i].ms,
+             "flops": arr[i].flops, "bytes": arr[i].bytes} for i in range(min(n.value, cap))]

@@ -24,7 +24,7 @@ MNS_NS_GRAM = 1
 EXPORTS = (
     "mns_status_string", "mns_version", "mns_step_workspace_size", "muon_step",
     "mns_ns_workspace_size", "ns_orthogonalize", "gram_ns_orthogonalize",
-    "mns_normuon_workspace_size", "normuon_scale",
+    "mns_normuon_workspace_size", "normuon_scale", "mns_profile_begin", "mns_profile_end",
 )
 
 
@@ -52,6 +52,16 @@ class MnsHparams(ctypes.Structure):
         ("eps", ctypes.c_float),
         ("row_fraction", ctypes.c_double),
         ("dtype", ctypes.c_int32),
+    ]
+
+
+class MnsKernelStat(ctypes.Structure):
+    _fields_ = [
+        ("name", ctypes.c_char * 64),
+        ("launches", ctypes.c_int64),
+        ("ms", ctypes.c_double),
+        ("flops", ctypes.c_double),
+        ("bytes", ctypes.c_double),
     ]
 
 
@@ -101,6 +111,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.normuon_scale.restype = ctypes.c_int
     lib.normuon_scale.argtypes = [vp, ctypes.c_int, i64, i64, i64, fp, ctypes.c_float,
                                   ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.mns_profile_begin.restype = ctypes.c_int
+    lib.mns_profile_begin.argtypes = []
+    lib.mns_profile_end.restype = ctypes.c_int
+    lib.mns_profile_end.argtypes = [ctypes.POINTER(MnsKernelStat), ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_int)]
     _lib = lib
     return lib
 

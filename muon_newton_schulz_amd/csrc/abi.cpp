@@ -10,11 +10,45 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <string>
 #include <vector>
 
 using namespace mns;
 
 namespace {
+
+// ---- instrumentation: hipEvent pairs around every launch while a session is open ----------
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+bool g_prof_failed = false;
+std::vector<ProfRec> g_prof;
+
+template <typename F>
+hipError_t timed(const char* name, double flops, double bytes, hipStream_t s, F&& launch) {
+  if (!g_prof_on) return launch();
+  ProfRec r{name, nullptr, nullptr, flops, bytes};
+  if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) {
+    g_prof_failed = true;
+    return launch();
+  }
+  hipEventRecord(r.a, s);
+  const hipError_t e = launch();
+  hipEventRecord(r.b, s);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back(r);
+  return e;
+}
+
+hipError_t timed_gemm(const GemmDesc& d, double flops, hipStream_t s) {
+  return timed(gemm_name(d), flops, 0.0, s, [&] { return gemm(d, s); });
+}
 
 constexpr int64_t kMaxDim = 65536;
 constexpr int64_t kMaxElems = 2147483647LL;
@@ -122,11 +156,12 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
   void* A = b.sq[0];
   void* B = b.sq[1];
   const float inv_s2 = 1.0f / (g.S * g.S);
+  const double nn = (double)count * g.n * g.n;
   for (int t = 0; t < T; ++t) {
     const float a = abc[3 * t], bb = abc[3 * t + 1], c = abc[3 * t + 2];
     GemmDesc gram = sym_desc(g, count, b, xin, xin, g.m_p, b.x_stride, (int)g.m_p, A);
     gram.alpha = inv_s2;
-    MNS_HIP(gemm(gram, s));
+    MNS_HIP(timed_gemm(gram, nn * g.m, s));
     const void* L = A;
     float lalpha = bb;
     if (c != 0.0f) {
@@ -134,7 +169,7 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
       poly.alpha = c;
       poly.beta = bb;
       poly.D = A; poly.ldd = g.n_p; poly.sD = b.sq_stride;
-      MNS_HIP(gemm(poly, s));
+      MNS_HIP(timed_gemm(poly, nn * g.n, s));
       L = B;
       lalpha = 1.0f;
     }
@@ -142,7 +177,7 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
     upd.alpha = lalpha;
     upd.beta = a;
     upd.D = xin; upd.ldd = g.m_p; upd.sD = b.x_stride;
-    MNS_HIP(gemm(upd, s));
+    MNS_HIP(timed_gemm(upd, 2.0 * nn * g.m, s));
     void* tmp = xin; xin = xout; xout = tmp;
   }
   *out = xin;
@@ -164,21 +199,22 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
   void* Qt = b.sq[5];
   const float inv_s2 = 1.0f / (g.S * g.S);
   const int n = (int)g.n_p;
+  const double nn = (double)count * g.n * g.n;
 
   GemmDesc gram = sym_desc(g, count, b, xcur, xcur, g.m_p, b.x_stride, (int)g.m_p, R);
   gram.alpha = inv_s2;
-  MNS_HIP(gemm(gram, s));
+  MNS_HIP(timed_gemm(gram, nn * g.m, s));
   bool q_identity = true;
   for (int t = 1; t <= T; ++t) {
     const float a = abc[3 * (t - 1)], bb = abc[3 * (t - 1) + 1], c = abc[3 * (t - 1) + 2];
     if (t > 1 && ((restart_mask >> t) & 1u)) {
       if (!q_identity) {
-        MNS_HIP(gemm(left_desc(g, count, b, Q, xcur, xoth), s));
+        MNS_HIP(timed_gemm(left_desc(g, count, b, Q, xcur, xoth), 2.0 * nn * g.m, s));
         void* tmp = xcur; xcur = xoth; xoth = tmp;
       }
       GemmDesc re = sym_desc(g, count, b, xcur, xcur, g.m_p, b.x_stride, (int)g.m_p, R);
       re.alpha = inv_s2;
-      MNS_HIP(gemm(re, s));
+      MNS_HIP(timed_gemm(re, nn * g.m, s));
       q_identity = true;
     }
     GemmDesc zd = sym_desc(g, count, b, R, R, g.n_p, b.sq_stride, n, Z);
@@ -187,24 +223,24 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
     zd.D = R; zd.ldd = g.n_p; zd.sD = b.sq_stride;
     zd.gamma = a;
     zd.diag_limit = (int)g.n;
-    MNS_HIP(gemm(zd, s));
+    MNS_HIP(timed_gemm(zd, nn * g.n, s));
     if (t < T && !((restart_mask >> (t + 1)) & 1u)) {
-      MNS_HIP(gemm(sym_desc(g, count, b, Z, Z, g.n_p, b.sq_stride, n, Z2), s));
-      MNS_HIP(gemm(sym_desc(g, count, b, R, Z2, g.n_p, b.sq_stride, n, Rt), s));
+      MNS_HIP(timed_gemm(sym_desc(g, count, b, Z, Z, g.n_p, b.sq_stride, n, Z2), nn * g.n, s));
+      MNS_HIP(timed_gemm(sym_desc(g, count, b, R, Z2, g.n_p, b.sq_stride, n, Rt), nn * g.n, s));
       void* tmp = R; R = Rt; Rt = tmp;
     }
     if (q_identity) {
       void* tmp = Q; Q = Z; Z = tmp;
       q_identity = false;
     } else {
-      MNS_HIP(gemm(sym_desc(g, count, b, Q, Z, g.n_p, b.sq_stride, n, Qt), s));
+      MNS_HIP(timed_gemm(sym_desc(g, count, b, Q, Z, g.n_p, b.sq_stride, n, Qt), nn * g.n, s));
       void* tmp = Q; Q = Qt; Qt = tmp;
     }
   }
   if (q_identity) {
     *out = xcur;
   } else {
-    MNS_HIP(gemm(left_desc(g, count, b, Q, xcur, xoth), s));
+    MNS_HIP(timed_gemm(left_desc(g, count, b, Q, xcur, xoth), 2.0 * nn * g.m, s));
     *out = xoth;
   }
   return MNS_OK;
@@ -409,33 +445,48 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
       StepWs w;
       carve_step(workspace, g, c, rows, cols, dion, k, hp->kind, w);
 
+      const double all = (double)c * rows * cols;      // elements of the chunk's matrices
+      const double sel = (double)c * k * cols;         // elements the NS runs on
+      const double es = elem_bytes(g.elem), ss = sto == Store::BF16 ? 2.0 : 4.0;
       if (!dion) {
-        MNS_HIP(momentum(Mp, Gp, sto, c, rows * cols, hp->mu, w.partials, s));
-        MNS_HIP(finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s));
-        MNS_HIP(normalize(&Mp, nullptr, true, sto, c, rows, cols, g.tall, w.xscale, g.elem,
-                          w.ns.X0, g.n_p, g.m_p, s));
+        MNS_HIP(timed("momentum", 0, all * (8.0 + ss), s, [&] {
+          return momentum(Mp, Gp, sto, c, rows * cols, hp->mu, w.partials, s); }));
+        MNS_HIP(timed("finalize_scale", 0, 4.0 * c * w.nblk, s, [&] {
+          return finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s); }));
+        MNS_HIP(timed("normalize", 0, all * (4.0 + es), s, [&] {
+          return normalize(&Mp, nullptr, true, sto, c, rows, cols, g.tall, w.xscale, g.elem,
+                           w.ns.X0, g.n_p, g.m_p, s); }));
       } else {
-        MNS_HIP(momentum_l1(Mp, Gp, sto, c, rows, cols, w.l1, s));
-        MNS_HIP(topk_rows(w.l1, c, rows, k, w.S, s));
-        MNS_HIP(gather_decay(Mp, c, cols, k, w.S, hp->mu, w.Msel, w.partials, s));
-        MNS_HIP(finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s));
-        MNS_HIP(normalize(nullptr, w.Msel, true, sto, c, k, cols, g.tall, w.xscale, g.elem,
-                          w.ns.X0, g.n_p, g.m_p, s));
+        MNS_HIP(timed("momentum_l1", 0, all * (8.0 + ss), s, [&] {
+          return momentum_l1(Mp, Gp, sto, c, rows, cols, w.l1, s); }));
+        MNS_HIP(timed("topk", 0, 4.0 * c * rows + 4.0 * c * k, s, [&] {
+          return topk_rows(w.l1, c, rows, k, w.S, s); }));
+        MNS_HIP(timed("gather_decay", 0, sel * 12.0, s, [&] {
+          return gather_decay(Mp, c, cols, k, w.S, hp->mu, w.Msel, w.partials, s); }));
+        MNS_HIP(timed("finalize_scale", 0, 4.0 * c * w.nblk, s, [&] {
+          return finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s); }));
+        MNS_HIP(timed("normalize", 0, sel * (4.0 + es), s, [&] {
+          return normalize(nullptr, w.Msel, true, sto, c, k, cols, g.tall, w.xscale, g.elem,
+                           w.ns.X0, g.n_p, g.m_p, s); }));
       }
       void* O = nullptr;
       st = run_ns(g, c, w.ns, hp->kind, hp->T, hp->abc, hp->restart_mask, s, &O);
       if (st != MNS_OK) return st;
       const float inv_s = 1.0f / g.S;
       if (hp->normuon) {
-        MNS_HIP(row_sumsq_x(O, g.elem, g.n_p, g.m_p, c, g.n, g.m, g.tall, w.part, s));
-        MNS_HIP(normuon_finalize(w.part, w.chunks, c, k, cols, &Vp, nullptr, 0,
-                                 dion ? w.S : nullptr, hp->beta2, hp->eps, inv_s * inv_s, inv_s,
-                                 w.rowscale, s));
+        MNS_HIP(timed("row_sumsq", 0, sel * es, s, [&] {
+          return row_sumsq_x(O, g.elem, g.n_p, g.m_p, c, g.n, g.m, g.tall, w.part, s); }));
+        MNS_HIP(timed("normuon_finalize", 0, 4.0 * c * k * (w.chunks + 3), s, [&] {
+          return normuon_finalize(w.part, w.chunks, c, k, cols, &Vp, nullptr, 0,
+                                  dion ? w.S : nullptr, hp->beta2, hp->eps, inv_s * inv_s, inv_s,
+                                  w.rowscale, s); }));
       } else {
-        MNS_HIP(fill(w.rowscale, (int64_t)c * k, inv_s, s));
+        MNS_HIP(timed("fill", 0, 4.0 * c * k, s, [&] {
+          return fill(w.rowscale, (int64_t)c * k, inv_s, s); }));
       }
-      MNS_HIP(weight_update(Wp, sto, c, k, cols, O, g.elem, g.n_p, g.m_p, g.tall, w.rowscale,
-                            dion ? w.S : nullptr, k, hp->lr, s));
+      MNS_HIP(timed("weight_update", 0, sel * (2.0 * ss + es) + 4.0 * c * k, s, [&] {
+        return weight_update(Wp, sto, c, k, cols, O, g.elem, g.n_p, g.m_p, g.tall, w.rowscale,
+                             dion ? w.S : nullptr, k, hp->lr, s); }));
     }
   }
   return MNS_OK;
@@ -495,14 +546,21 @@ static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch
     ns_bytes(g, c, kind, rows, cols, &nb, &partials, &xscale, ws);
     const char* xin = static_cast<const char*>(X) + (size_t)b0 * rows * cols * esz;
     char* out = static_cast<char*>(O) + (size_t)b0 * rows * cols * esz;
-    MNS_HIP(sumsq(xin, sto, c, rows * cols, partials, s));
-    MNS_HIP(finalize_scale(partials, norm_blocks(rows * cols), c, g.S, xscale, s));
-    MNS_HIP(normalize(nullptr, xin, false, sto, c, rows, cols, g.tall, xscale, g.elem, nb.X0,
-                      g.n_p, g.m_p, s));
+    const double all = (double)c * rows * cols, ss = (double)esz, es = elem_bytes(g.elem);
+    const int nblk = norm_blocks(rows * cols);
+    MNS_HIP(timed("sumsq", 0, all * ss, s, [&] {
+      return sumsq(xin, sto, c, rows * cols, partials, s); }));
+    MNS_HIP(timed("finalize_scale", 0, 4.0 * c * nblk, s, [&] {
+      return finalize_scale(partials, nblk, c, g.S, xscale, s); }));
+    MNS_HIP(timed("normalize", 0, all * (ss + es), s, [&] {
+      return normalize(nullptr, xin, false, sto, c, rows, cols, g.tall, xscale, g.elem, nb.X0,
+                       g.n_p, g.m_p, s); }));
     void* res = nullptr;
     st = run_ns(g, c, nb, kind, T, abc, restart_mask, s, &res);
     if (st != MNS_OK) return st;
-    MNS_HIP(export_output(res, g.elem, g.n_p, g.m_p, c, rows, cols, g.tall, 1.0f / g.S, out, sto, s));
+    MNS_HIP(timed("export", 0, all * (ss + es), s, [&] {
+      return export_output(res, g.elem, g.n_p, g.m_p, c, rows, cols, g.tall, 1.0f / g.S, out,
+                           sto, s); }));
   }
   return MNS_OK;
 }
@@ -558,11 +616,59 @@ mns_status normuon_scale(void* O, int dtype, int64_t batch, int64_t rows, int64_
   const Store sto = dtype == MNS_BF16 ? Store::BF16 : Store::F32;
   float *part = nullptr, *rowscale = nullptr;
   normuon_bytes(batch, rows, &part, &rowscale, workspace);
-  MNS_HIP(row_sumsq_stored(O, sto, (int)batch, rows, cols, part, s));
-  MNS_HIP(normuon_finalize(part, 1, (int)batch, rows, cols, nullptr, v, rows, nullptr, beta2, eps,
-                           1.0f, 1.0f, rowscale, s));
-  MNS_HIP(rowscale_apply(O, sto, (int)batch, rows, cols, rowscale, s));
+  const double all = (double)batch * rows * cols, ss = sto == Store::BF16 ? 2.0 : 4.0;
+  MNS_HIP(timed("row_sumsq_stored", 0, all * ss, s, [&] {
+    return row_sumsq_stored(O, sto, (int)batch, rows, cols, part, s); }));
+  MNS_HIP(timed("normuon_finalize", 0, 4.0 * batch * rows * 4, s, [&] {
+    return normuon_finalize(part, 1, (int)batch, rows, cols, nullptr, v, rows, nullptr, beta2,
+                            eps, 1.0f, 1.0f, rowscale, s); }));
+  MNS_HIP(timed("rowscale_apply", 0, 2.0 * all * ss, s, [&] {
+    return rowscale_apply(O, sto, (int)batch, rows, cols, rowscale, s); }));
   return MNS_OK;
+}
+
+mns_status mns_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (ProfRec& r : g_prof) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  g_prof_failed = false;
+  g_prof_on = true;
+  return MNS_OK;
+}
+
+mns_status mns_profile_end(mns_kernel_stat* out, int capacity, int* count) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return MNS_ERR_PARAM;
+  g_prof_on = false;
+  std::vector<mns_kernel_stat> stats;
+  bool ok = !g_prof_failed;
+  for (ProfRec& r : g_prof) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      ok = false;
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+    mns_kernel_stat* st = nullptr;
+    for (auto& x : stats)
+      if (std::strncmp(x.name, r.name, sizeof(x.name)) == 0) st = &x;
+    if (!st) {
+      mns_kernel_stat z = {};
+      std::strncpy(z.name, r.name, sizeof(z.name) - 1);
+      stats.push_back(z);
+      st = &stats.back();
+    }
+    st->launches += 1;
+    st->ms += ms;
+    st->flops += r.flops;
+    st->bytes += r.bytes;
+  }
+  g_prof.clear();
+  if (count) *count = (int)stats.size();
+  for (int i = 0; i < (int)stats.size() && i < capacity && out; ++i) out[i] = stats[i];
+  return ok ? MNS_OK : MNS_ERR_HIP;
 }
 
 }  // extern "C"

@@ -326,15 +326,28 @@ hipError_t dispatch_tile(const GemmDesc& d, hipStream_t s) {
 
 }  // namespace
 
+// 256 x 256 tiles when they give at least two waves of blocks over the 256 CUs.
+static int tile_for(const GemmDesc& d) {
+  if (d.elem == Elem::F32) return 128;
+  const int64_t t256 = d.sym ? (int64_t)(d.M / 256) * (d.M / 256 + 1) / 2
+                             : (int64_t)(d.M / 256) * (d.N / 256);
+  return t256 * d.batch >= 512 ? 256 : 128;
+}
+
 hipError_t gemm(const GemmDesc& d, hipStream_t s) {
   if (d.M % kPad || d.N % kPad || d.K % kPad || d.batch < 1) return hipErrorInvalidValue;
   if (d.sym && (d.M != d.N || !d.b_kmajor)) return hipErrorInvalidValue;
   if (d.elem == Elem::F32) return dispatch_tile<float, 128>(d, s);
-  // 256 x 256 tiles when they give at least two waves of blocks over the 256 CUs.
-  const int64_t t256 = d.sym ? (int64_t)(d.M / 256) * (d.M / 256 + 1) / 2
-                             : (int64_t)(d.M / 256) * (d.N / 256);
-  if (t256 * d.batch >= 512) return dispatch_tile<_Float16, 256>(d, s);
+  if (tile_for(d) == 256) return dispatch_tile<_Float16, 256>(d, s);
   return dispatch_tile<_Float16, 128>(d, s);
+}
+
+const char* gemm_name(const GemmDesc& d) {
+  const bool f32 = d.elem == Elem::F32;
+  const bool t256 = tile_for(d) == 256;
+  if (d.sym) return f32 ? "gemm_sym_f32_128" : (t256 ? "gemm_sym_f16_256" : "gemm_sym_f16_128");
+  if (d.b_kmajor) return f32 ? "gemm_nt_f32_128" : (t256 ? "gemm_nt_f16_256" : "gemm_nt_f16_128");
+  return f32 ? "gemm_nn_f32_128" : (t256 ? "gemm_nn_f16_256" : "gemm_nn_f16_128");
 }
 
 }  // namespace mns

@@ -51,6 +51,8 @@ struct GemmDesc {
   bool sym = false;
 };
 hipError_t gemm(const GemmDesc& d, hipStream_t s);
+// Name of the kernel instantiation gemm() launches for this descriptor.
+const char* gemm_name(const GemmDesc& d);
 
 // ---------------------------------------------------------------------------------------
 // Elementwise / reduction kernels (elementwise.hip). All are deterministic: fixed
