@@ -34,7 +34,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
 constexpr int kChunks = 8;   // 16-byte chunks per LDS row (one 128-byte k-tile)
 
 template <typename T>
@@ -47,21 +46,6 @@ struct Traits<_Float16> {
   __device__ static __forceinline__ void mma(floatx16& acc, u32x4 a, u32x4 b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
                                                  __builtin_bit_cast(half8, b), acc, 0, 0, 0);
-  }
-  // 8 x 8 transpose of 16-bit elements: in[r] holds row r (8 elements of the n axis),
-  // out[e] holds column e (8 elements of the k axis, k = 0..7 from in[0..7]).
-  __device__ static __forceinline__ void transpose(const u32x4* in, u32x4* out) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = e >> 1;
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const unsigned lo = in[2 * q][d], hi = in[2 * q + 1][d];
-        o[q] = (e & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-      }
-      out[e] = o;
-    }
   }
 };
 
@@ -77,15 +61,6 @@ struct Traits<float> {
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[p]), __uint_as_float(b[p]),
                                                  acc, 0, 0, 0);
   }
-  __device__ static __forceinline__ void transpose(const u32x4* in, u32x4* out) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = in[q][e];
-      out[e] = o;
-    }
-  }
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) {
@@ -100,6 +75,7 @@ struct GemmArgs {
   float alpha, beta, gamma;
   int diag_limit;
   int tiles_n;      // N / BN (dense grid) or tiles per side (sym)
+  int group;        // tile rows per group of the dense tile order
 };
 
 template <typename T>
@@ -127,38 +103,66 @@ __device__ __forceinline__ void load4<float>(const float* p, float* v) {
   v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
 }
 
-template <typename T, int BM, int BN, bool BKMAJ, bool SYM>
-__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs p) {
+// Block tile BM x BN computed by WGM x WGN waves (wave tile BM/WGM x BN/WGN).
+template <typename T, int BM, int BN, int WGM, int WGN, bool BKMAJ, bool SYM>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   using Tr = Traits<T>;
+  constexpr int NT = 64 * WGM * WGN;
   constexpr int VEC = Tr::VEC, BK = Tr::BK;
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  constexpr int A_LD = BM * kChunks / kThreads;            // A chunks per thread
-  constexpr int BK_LD = BN * kChunks / kThreads;           // k-major B chunks per thread
-  constexpr int NN_BLK = kChunks * BN / VEC;               // VEC x VEC blocks of an [K][N] tile
-  constexpr int NN_PER = (NN_BLK + kThreads - 1) / kThreads;
-  constexpr int B_REGS = BKMAJ ? BK_LD : NN_PER * VEC;
-  static_assert(A_LD >= 1 && BK_LD >= 1, "tile too small");
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+  constexpr int A_LD = BM * kChunks / NT;                  // A chunks per thread
+  constexpr int BK_LD = BN * kChunks / NT;                 // k-major B chunks per thread
+  // [K][N] operand: a thread loads 4 k-rows x VEC n-columns (4 x 16 bytes) per k-tile.
+  constexpr int NN_JOBS = (BK / 4) * (BN / VEC);
+  constexpr int B_REGS = BKMAJ ? BK_LD : 4;
+  static_assert(A_LD >= 1 && BK_LD >= 1 && FM >= 1 && FN >= 1, "tile too small");
+  static_assert(BKMAJ || NN_JOBS == NT, "[K][N] loader assumes one 4-row job per thread");
 
   __shared__ u32x4 lds[2][(BM + BN) * kChunks];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
+  // Tile order. Workgroups go round-robin to the 8 XCDs (L2 domains); remap so each XCD
+  // walks a contiguous range of logical tiles, and order those in groups of p.group tile
+  // rows (column-major inside a group), so the CUs of one XCD share A rows and B columns.
+  int t = blockIdx.x;
+  {
+    const int q = (int)gridDim.x / 8;
+    if (t < 8 * q) t = (t % 8) * q + t / 8;
+  }
   int tm, tn;
   if (SYM) {
-    int r = blockIdx.x;
     tm = 0;
-    while (r >= p.tiles_n - tm) { r -= p.tiles_n - tm; ++tm; }
-    tn = tm + r;
+    while (t >= p.tiles_n - tm) { t -= p.tiles_n - tm; ++tm; }
+    tn = tm + t;
   } else {
-    tm = blockIdx.x / p.tiles_n;
-    tn = blockIdx.x % p.tiles_n;
+    const int tiles_m = p.M / BM;
+    const int per_group = p.group * p.tiles_n;
+    const int g = t / per_group, l = t % per_group;
+    const int first = g * p.group;
+    const int gsize = tiles_m - first < p.group ? tiles_m - first : p.group;
+    tm = first + l % gsize;
+    tn = l / gsize;
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int64_t bz = blockIdx.z;
   const T* Ag = static_cast<const T*>(p.A) + bz * p.sA + (int64_t)m0 * p.lda;
   const T* Bg = static_cast<const T*>(p.B) + bz * p.sB +
                 (BKMAJ ? (int64_t)n0 * p.ldb : (int64_t)n0);
+
+  // [K][N] job of this thread: 16-bit types alternate the 8-byte half of the k-chunk
+  // between neighbouring lanes, which keeps the 8-byte LDS writes conflict-free.
+  int nn_c = 0, nn_kq = 0;
+  if (!BKMAJ) {
+    if (VEC == 8) {
+      nn_c = (tid >> 1) % (BN / VEC);
+      nn_kq = 2 * ((tid >> 1) / (BN / VEC)) + (tid & 1);
+    } else {
+      nn_c = tid % (BN / VEC);
+      nn_kq = tid / (BN / VEC);
+    }
+  }
 
   u32x4 ra[A_LD];
   u32x4 rb[B_REGS];
@@ -167,53 +171,63 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs p) {
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const int q = tid + kThreads * i, row = q / kChunks, ch = q % kChunks;
+      const int q = tid + NT * i, row = q / kChunks, ch = q % kChunks;
       ra[i] = *reinterpret_cast<const u32x4*>(Ag + (int64_t)row * p.lda + k0 + ch * VEC);
     }
     if (BKMAJ) {
 #pragma unroll
       for (int i = 0; i < BK_LD; ++i) {
-        const int q = tid + kThreads * i, row = q / kChunks, ch = q % kChunks;
+        const int q = tid + NT * i, row = q / kChunks, ch = q % kChunks;
         rb[i] = *reinterpret_cast<const u32x4*>(Bg + (int64_t)row * p.ldb + k0 + ch * VEC);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < NN_PER; ++i) {
-        const int qb = tid + kThreads * i;
-        if (NN_BLK % kThreads == 0 || qb < NN_BLK) {
-          const int nc = qb % (BN / VEC), kg = qb / (BN / VEC);
-#pragma unroll
-          for (int r = 0; r < VEC; ++r)
-            rb[i * VEC + r] = *reinterpret_cast<const u32x4*>(
-                Bg + (int64_t)(k0 + kg * VEC + r) * p.ldb + nc * VEC);
-        }
-      }
+      for (int r = 0; r < 4; ++r)
+        rb[r] = *reinterpret_cast<const u32x4*>(Bg + (int64_t)(k0 + 4 * nn_kq + r) * p.ldb +
+                                               nn_c * VEC);
     }
   };
 
   auto store_lds = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const int q = tid + kThreads * i, row = q / kChunks, ch = q % kChunks;
+      const int q = tid + NT * i, row = q / kChunks, ch = q % kChunks;
       lds[buf][swz(row, ch)] = ra[i];
     }
     if (BKMAJ) {
 #pragma unroll
       for (int i = 0; i < BK_LD; ++i) {
-        const int q = tid + kThreads * i, row = q / kChunks, ch = q % kChunks;
+        const int q = tid + NT * i, row = q / kChunks, ch = q % kChunks;
         lds[buf][swz(BM + row, ch)] = rb[i];
       }
-    } else {
+    } else if (VEC == 8) {
+      // 4 k-rows x 8 n-columns of 16-bit values -> for each column e, 4 consecutive k
+      // (8 bytes) into half (nn_kq & 1) of k-chunk nn_kq / 2 of LDS row n.
+      unsigned* base = reinterpret_cast<unsigned*>(&lds[buf][0]);
 #pragma unroll
-      for (int i = 0; i < NN_PER; ++i) {
-        const int qb = tid + kThreads * i;
-        if (NN_BLK % kThreads == 0 || qb < NN_BLK) {
-          const int nc = qb % (BN / VEC), kg = qb / (BN / VEC);
-          u32x4 t[VEC];
-          Tr::transpose(&rb[i * VEC], t);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) lds[buf][swz(BM + nc * VEC + e, kg)] = t[e];
+      for (int e = 0; e < 8; ++e) {
+        const int d = e >> 1;
+        const unsigned r0 = rb[0][d], r1 = rb[1][d], r2 = rb[2][d], r3 = rb[3][d];
+        unsigned w0, w1;
+        if (e & 1) {
+          w0 = (r0 >> 16) | (r1 & 0xFFFF0000u);
+          w1 = (r2 >> 16) | (r3 & 0xFFFF0000u);
+        } else {
+          w0 = (r0 & 0xFFFFu) | (r1 << 16);
+          w1 = (r2 & 0xFFFFu) | (r3 << 16);
         }
+        const int row = BM + nn_c * 8 + e;
+        unsigned* dst = base + 4 * swz(row, nn_kq >> 1) + 2 * (nn_kq & 1);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+      }
+    } else {
+      // 4 k-rows x 4 n-columns of float32 -> one 16-byte k-chunk per column.
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = rb[q][e];
+        lds[buf][swz(BM + nn_c * 4 + e, nn_kq)] = o;
       }
     }
   };
@@ -226,30 +240,39 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  const int arow = wm * WM + (lane & 31);
+  const int brow = BM + wn * WN + (lane & 31);
+  u32x4 af[2][FM], bf[2][FN];
+  auto load_frags = [&](int buf, int ks, int slot) {
+    const int ch = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[slot][i] = lds[buf][swz(arow + 32 * i, ch)];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bf[slot][j] = lds[buf][swz(brow + 32 * j, ch)];
+  };
+
+  // Pipeline: LDS holds tile kt (being read) and receives tile kt+1 from registers at the
+  // top of iteration kt; the registers are then refilled with tile kt+2, so every global
+  // load has a whole iteration of MFMA work to arrive.
   const int KT = p.K / BK;
   load_global(0);
   store_lds(0);
+  if (KT > 1) load_global(1);
   __syncthreads();
 
-  const int arow = wm * WM + (lane & 31);
-  const int brow = BM + wn * WN + (lane & 31);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) load_global(kt + 1);
+    load_frags(cur, 0, 0);
+    if (kt + 1 < KT) store_lds(cur ^ 1);
+    if (kt + 2 < KT) load_global(kt + 2);
 #pragma unroll
     for (int ks = 0; ks < kChunks / 2; ++ks) {
-      const int ch = 2 * ks + (lane >> 5);
-      u32x4 af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = lds[cur][swz(arow + 32 * i, ch)];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bf[j] = lds[cur][swz(brow + 32 * j, ch)];
+      if (ks + 1 < kChunks / 2) load_frags(cur, ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) Tr::mma(acc[i][j], bf[j], af[i]);
+        for (int j = 0; j < FN; ++j) Tr::mma(acc[i][j], bf[ks & 1][j], af[ks & 1][i]);
     }
-    if (kt + 1 < KT) store_lds(cur ^ 1);
     __syncthreads();
   }
 
@@ -294,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs p) {
   }
 }
 
-template <typename T, int BM, int BN, bool BKMAJ, bool SYM>
+template <typename T, int BM, int BN, int WGM, int WGN, bool BKMAJ, bool SYM>
 hipError_t launch(const GemmDesc& d, hipStream_t s) {
   GemmArgs a;
   a.A = d.A; a.B = d.B; a.C = d.C; a.D = d.D;
@@ -303,6 +326,7 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   a.M = d.M; a.N = d.N; a.K = d.K;
   a.alpha = d.alpha; a.beta = d.beta; a.gamma = d.gamma;
   a.diag_limit = d.diag_limit;
+  a.group = 4;
   unsigned tiles;
   if (SYM) {
     const int t = d.M / BM;
@@ -312,16 +336,16 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
     a.tiles_n = d.N / BN;
     tiles = (unsigned)((d.M / BM) * (d.N / BN));
   }
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, BKMAJ, SYM>), dim3(tiles, 1, d.batch), dim3(kThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, BKMAJ, SYM>), dim3(tiles, 1, d.batch),
+                     dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, int BT>
+template <typename T, int BT, int WGM, int WGN>
 hipError_t dispatch_tile(const GemmDesc& d, hipStream_t s) {
-  if (d.sym) return launch<T, BT, BT, true, true>(d, s);
-  if (d.b_kmajor) return launch<T, BT, BT, true, false>(d, s);
-  return launch<T, BT, BT, false, false>(d, s);
+  if (d.sym) return launch<T, BT, BT, WGM, WGN, true, true>(d, s);
+  if (d.b_kmajor) return launch<T, BT, BT, WGM, WGN, true, false>(d, s);
+  return launch<T, BT, BT, WGM, WGN, false, false>(d, s);
 }
 
 }  // namespace
@@ -337,9 +361,9 @@ static int tile_for(const GemmDesc& d) {
 hipError_t gemm(const GemmDesc& d, hipStream_t s) {
   if (d.M % kPad || d.N % kPad || d.K % kPad || d.batch < 1) return hipErrorInvalidValue;
   if (d.sym && (d.M != d.N || !d.b_kmajor)) return hipErrorInvalidValue;
-  if (d.elem == Elem::F32) return dispatch_tile<float, 128>(d, s);
-  if (tile_for(d) == 256) return dispatch_tile<_Float16, 256>(d, s);
-  return dispatch_tile<_Float16, 128>(d, s);
+  if (d.elem == Elem::F32) return dispatch_tile<float, 128, 2, 2>(d, s);
+  if (tile_for(d) == 256) return dispatch_tile<_Float16, 256, 2, 4>(d, s);
+  return dispatch_tile<_Float16, 128, 2, 2>(d, s);
 }
 
 const char* gemm_name(const GemmDesc& d) {
