@@ -38,9 +38,9 @@ hipError_t timed(const char* name, double flops, double bytes, hipStream_t s, F&
     g_prof_failed = true;
     return launch();
   }
-  hipEventRecord(r.a, s);
+  (void)hipEventRecord(r.a, s);
   const hipError_t e = launch();
-  hipEventRecord(r.b, s);
+  (void)hipEventRecord(r.b, s);
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof.push_back(r);
   return e;
@@ -75,6 +75,7 @@ struct Carver {
 // its entries well inside the normal range: X_0 entries ~ S/sqrt(nm), later ~ S/sqrt(m)).
 struct Geo {
   int64_t rows, cols, n, m, n_p, m_p;
+  int64_t rows_p, cols_p;      // stored layout, padded (the result O is kept this way)
   bool tall;
   Elem elem;
   float S;
@@ -89,6 +90,8 @@ Geo make_geo(int64_t rows, int64_t cols, Store st) {
   g.m = g.tall ? rows : cols;
   g.n_p = pad_up(g.n);
   g.m_p = pad_up(g.m);
+  g.rows_p = pad_up(rows);
+  g.cols_p = pad_up(cols);
   g.elem = st == Store::BF16 ? Elem::F16 : Elem::F32;
   if (g.elem == Elem::F16) {
     int e = (int)std::lround(0.5 * std::log2((double)g.m));
@@ -101,9 +104,11 @@ Geo make_geo(int64_t rows, int64_t cols, Store st) {
   return g;
 }
 
+// The iterate is kept in two layouts: X (n_p x m_p, rows = the short side) feeds X X^T and
+// X^T (m_p x n_p) feeds the k-contiguous operand of B X and Q X; each has a ping-pong pair.
 struct NsBuffers {
-  void* X0 = nullptr;
-  void* X1 = nullptr;
+  void* X[2] = {};
+  void* Xt[2] = {};
   void* sq[6] = {};        // n_p x n_p scratch: standard uses 2, Gram uses 6
   int64_t x_stride = 0, sq_stride = 0;
 };
@@ -112,11 +117,18 @@ void carve_ns(Carver& cv, const Geo& g, int count, int kind, NsBuffers& b) {
   const size_t es = (size_t)elem_bytes(g.elem);
   b.x_stride = g.n_p * g.m_p;
   b.sq_stride = g.n_p * g.n_p;
-  b.X0 = cv.take<char>(es * count * b.x_stride);
-  b.X1 = cv.take<char>(es * count * b.x_stride);
+  for (int i = 0; i < 2; ++i) {
+    b.X[i] = cv.take<char>(es * count * b.x_stride);
+    b.Xt[i] = cv.take<char>(es * count * b.x_stride);
+  }
   const int nsq = kind == MNS_NS_GRAM ? 6 : 2;
   for (int i = 0; i < nsq; ++i) b.sq[i] = cv.take<char>(es * count * b.sq_stride);
 }
+
+// Normalisation targets: the stored layout of the source is X for a wide matrix and X^T for
+// a tall one; the other buffer receives the transpose.
+void* straight(const Geo& g, const NsBuffers& b) { return g.tall ? b.Xt[0] : b.X[0]; }
+void* transposed(const Geo& g, const NsBuffers& b) { return g.tall ? b.X[0] : b.Xt[0]; }
 
 #define MNS_HIP(expr)                               \
   do {                                              \
@@ -128,38 +140,40 @@ GemmDesc sym_desc(const Geo& g, int count, const NsBuffers& b, const void* A, co
   GemmDesc d;
   d.elem = g.elem;
   d.A = A; d.lda = ldab; d.sA = sab;
-  d.B = B; d.ldb = ldab; d.sB = sab; d.b_kmajor = true;
+  d.B = B; d.ldb = ldab; d.sB = sab;
   d.C = C; d.ldc = g.n_p; d.sC = b.sq_stride;
   d.M = (int)g.n_p; d.N = (int)g.n_p; d.K = K; d.batch = count;
   d.sym = true;
   return d;
 }
 
-// C (n_p x m_p) = alpha * L X + beta * D, L: n_p x n_p, X: n_p x m_p (n-contiguous operand).
-GemmDesc left_desc(const Geo& g, int count, const NsBuffers& b, const void* L, const void* X,
-                   void* C) {
+// L X for L n_p x n_p (symmetric) and X given by its transpose Xt (m_p x n_p): written to
+// C (n_p x m_p) and/or Ct (m_p x n_p).
+GemmDesc left_desc(const Geo& g, int count, const NsBuffers& b, const void* L, const void* Xt,
+                   void* C, void* Ct) {
   GemmDesc d;
   d.elem = g.elem;
   d.A = L; d.lda = g.n_p; d.sA = b.sq_stride;
-  d.B = X; d.ldb = g.m_p; d.sB = b.x_stride; d.b_kmajor = false;
+  d.B = Xt; d.ldb = g.n_p; d.sB = b.x_stride;
   d.C = C; d.ldc = g.m_p; d.sC = b.x_stride;
+  d.Ct = Ct; d.ldct = g.n_p; d.sCt = b.x_stride;
   d.M = (int)g.n_p; d.N = (int)g.m_p; d.K = (int)g.n_p; d.batch = count;
   return d;
 }
 
-// Standard quintic NS on the normalised iterate in b.X0 (section "Standard Newton-Schulz"):
-// A = X X^T, B = b A + c A^2, X <- a X + B X. Returns the buffer holding X_T.
+// Standard quintic NS on the normalised iterate (b.X[0], b.Xt[0]) (section "Standard
+// Newton-Schulz"): A = X X^T, B = b A + c A^2, X <- a X + B X. Returns the result in the
+// stored layout (X for a wide matrix, X^T for a tall one; leading dimension cols_p).
 mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, const float* abc,
                         hipStream_t s, void** out) {
-  void* xin = b.X0;
-  void* xout = b.X1;
+  int cur = 0;
   void* A = b.sq[0];
   void* B = b.sq[1];
   const float inv_s2 = 1.0f / (g.S * g.S);
   const double nn = (double)count * g.n * g.n;
   for (int t = 0; t < T; ++t) {
     const float a = abc[3 * t], bb = abc[3 * t + 1], c = abc[3 * t + 2];
-    GemmDesc gram = sym_desc(g, count, b, xin, xin, g.m_p, b.x_stride, (int)g.m_p, A);
+    GemmDesc gram = sym_desc(g, count, b, b.X[cur], b.X[cur], g.m_p, b.x_stride, (int)g.m_p, A);
     gram.alpha = inv_s2;
     MNS_HIP(timed_gemm(gram, nn * g.m, s));
     const void* L = A;
@@ -173,24 +187,25 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
       L = B;
       lalpha = 1.0f;
     }
-    GemmDesc upd = left_desc(g, count, b, L, xin, xout);
+    const bool last = t == T - 1;
+    GemmDesc upd = left_desc(g, count, b, L, b.Xt[cur], (!last || !g.tall) ? b.X[cur ^ 1] : nullptr,
+                             (!last || g.tall) ? b.Xt[cur ^ 1] : nullptr);
     upd.alpha = lalpha;
     upd.beta = a;
-    upd.D = xin; upd.ldd = g.m_p; upd.sD = b.x_stride;
+    upd.D = b.X[cur]; upd.ldd = g.m_p; upd.sD = b.x_stride;   // read in C coordinates
     MNS_HIP(timed_gemm(upd, 2.0 * nn * g.m, s));
-    void* tmp = xin; xin = xout; xout = tmp;
+    cur ^= 1;
   }
-  *out = xin;
+  *out = g.tall ? b.Xt[cur] : b.X[cur];
   return MNS_OK;
 }
 
 // Gram Newton-Schulz (Theorem 2) with restarts (Algorithm 3): R = X X^T; per iteration
 // Z = a I + b R + c R^2, R <- R Z^2 (skipped when unused), Q <- Q Z (Q_1 = Z_1);
-// a restart before t forms X <- Q X, R <- X X^T, Q <- I. Output Q X.
+// a restart before t forms X <- Q X, R <- X X^T, Q <- I. Output Q X (stored layout).
 mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const float* abc,
                     uint32_t restart_mask, hipStream_t s, void** out) {
-  void* xcur = b.X0;
-  void* xoth = b.X1;
+  int cur = 0;
   void* R = b.sq[0];
   void* Rt = b.sq[1];
   void* Z = b.sq[2];
@@ -201,7 +216,7 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
   const int n = (int)g.n_p;
   const double nn = (double)count * g.n * g.n;
 
-  GemmDesc gram = sym_desc(g, count, b, xcur, xcur, g.m_p, b.x_stride, (int)g.m_p, R);
+  GemmDesc gram = sym_desc(g, count, b, b.X[cur], b.X[cur], g.m_p, b.x_stride, (int)g.m_p, R);
   gram.alpha = inv_s2;
   MNS_HIP(timed_gemm(gram, nn * g.m, s));
   bool q_identity = true;
@@ -209,10 +224,11 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
     const float a = abc[3 * (t - 1)], bb = abc[3 * (t - 1) + 1], c = abc[3 * (t - 1) + 2];
     if (t > 1 && ((restart_mask >> t) & 1u)) {
       if (!q_identity) {
-        MNS_HIP(timed_gemm(left_desc(g, count, b, Q, xcur, xoth), 2.0 * nn * g.m, s));
-        void* tmp = xcur; xcur = xoth; xoth = tmp;
+        MNS_HIP(timed_gemm(left_desc(g, count, b, Q, b.Xt[cur], b.X[cur ^ 1], b.Xt[cur ^ 1]),
+                           2.0 * nn * g.m, s));
+        cur ^= 1;
       }
-      GemmDesc re = sym_desc(g, count, b, xcur, xcur, g.m_p, b.x_stride, (int)g.m_p, R);
+      GemmDesc re = sym_desc(g, count, b, b.X[cur], b.X[cur], g.m_p, b.x_stride, (int)g.m_p, R);
       re.alpha = inv_s2;
       MNS_HIP(timed_gemm(re, nn * g.m, s));
       q_identity = true;
@@ -238,10 +254,12 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
     }
   }
   if (q_identity) {
-    *out = xcur;
+    *out = g.tall ? b.Xt[cur] : b.X[cur];
   } else {
-    MNS_HIP(timed_gemm(left_desc(g, count, b, Q, xcur, xoth), 2.0 * nn * g.m, s));
-    *out = xoth;
+    MNS_HIP(timed_gemm(left_desc(g, count, b, Q, b.Xt[cur], g.tall ? nullptr : b.X[cur ^ 1],
+                                 g.tall ? b.Xt[cur ^ 1] : nullptr),
+                       2.0 * nn * g.m, s));
+    *out = g.tall ? b.Xt[cur ^ 1] : b.X[cur ^ 1];
   }
   return MNS_OK;
 }
@@ -261,6 +279,12 @@ mns_status check_shape(int64_t batch, int64_t rows, int64_t cols) {
   if (rows > kMaxDim || cols > kMaxDim || rows * cols > kMaxElems) return MNS_ERR_SHAPE;
   if (batch > kMaxElems / (rows * cols)) return MNS_ERR_SHAPE;
   return MNS_OK;
+}
+
+// The GEMMs address one padded iterate with 32-bit byte offsets.
+mns_status check_iterate(int64_t rows, int64_t cols, Store st) {
+  const int64_t bytes = pad_up(rows) * pad_up(cols) * (st == Store::BF16 ? 2 : 4);
+  return bytes <= kMaxElems ? MNS_OK : MNS_ERR_SHAPE;
 }
 
 mns_status check_dtype(int dt) {
@@ -332,6 +356,8 @@ mns_status validate_step(const mns_matrix* mats, int count, const mns_hparams* h
   for (int i = 0; i < count; ++i) {
     st = check_shape(1, mats[i].rows, mats[i].cols);
     if (st != MNS_OK) return st;
+    st = check_iterate(mats[i].rows, mats[i].cols, hp->dtype == MNS_BF16 ? Store::BF16 : Store::F32);
+    if (st != MNS_OK) return st;
     if (need_ptrs) {
       if (!mats[i].W || !mats[i].M || !mats[i].G) return MNS_ERR_NULL;
       if (hp->normuon && !mats[i].v) return MNS_ERR_NULL;
@@ -363,10 +389,9 @@ size_t carve_step(void* base, const Geo& g, int count, int64_t rows, int64_t col
   w.partials = cv.take<float>((size_t)count * w.nblk);
   w.xscale = cv.take<float>((size_t)count);
   carve_ns(cv, g, count, kind, w.ns);
-  const int64_t stored_rows = g.tall ? g.m : g.n;     // rows of the matrix NS ran on
-  w.chunks = (int)((g.tall ? g.n_p : g.m_p) / kPad);
-  w.part = cv.take<float>((size_t)count * w.chunks * stored_rows);
-  w.rowscale = cv.take<float>((size_t)count * stored_rows);
+  w.chunks = (int)(g.cols_p / kPad);                   // row-norm partials per stored row
+  w.part = cv.take<float>((size_t)count * w.chunks * g.rows);
+  w.rowscale = cv.take<float>((size_t)count * g.rows);
   if (dion) {
     w.l1 = cv.take<float>((size_t)count * rows);
     w.S = cv.take<int32_t>((size_t)count * k);
@@ -453,9 +478,9 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
           return momentum(Mp, Gp, sto, c, rows * cols, hp->mu, w.partials, s); }));
         MNS_HIP(timed("finalize_scale", 0, 4.0 * c * w.nblk, s, [&] {
           return finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s); }));
-        MNS_HIP(timed("normalize", 0, all * (4.0 + es), s, [&] {
-          return normalize(&Mp, nullptr, true, sto, c, rows, cols, g.tall, w.xscale, g.elem,
-                           w.ns.X0, g.n_p, g.m_p, s); }));
+        MNS_HIP(timed("normalize", 0, all * (4.0 + 2.0 * es), s, [&] {
+          return normalize(&Mp, nullptr, true, sto, c, rows, cols, w.xscale, g.elem,
+                           straight(g, w.ns), transposed(g, w.ns), g.rows_p, g.cols_p, s); }));
       } else {
         MNS_HIP(timed("momentum_l1", 0, all * (8.0 + ss), s, [&] {
           return momentum_l1(Mp, Gp, sto, c, rows, cols, w.l1, s); }));
@@ -465,9 +490,9 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
           return gather_decay(Mp, c, cols, k, w.S, hp->mu, w.Msel, w.partials, s); }));
         MNS_HIP(timed("finalize_scale", 0, 4.0 * c * w.nblk, s, [&] {
           return finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s); }));
-        MNS_HIP(timed("normalize", 0, sel * (4.0 + es), s, [&] {
-          return normalize(nullptr, w.Msel, true, sto, c, k, cols, g.tall, w.xscale, g.elem,
-                           w.ns.X0, g.n_p, g.m_p, s); }));
+        MNS_HIP(timed("normalize", 0, sel * (4.0 + 2.0 * es), s, [&] {
+          return normalize(nullptr, w.Msel, true, sto, c, k, cols, w.xscale, g.elem,
+                           straight(g, w.ns), transposed(g, w.ns), g.rows_p, g.cols_p, s); }));
       }
       void* O = nullptr;
       st = run_ns(g, c, w.ns, hp->kind, hp->T, hp->abc, hp->restart_mask, s, &O);
@@ -475,7 +500,7 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
       const float inv_s = 1.0f / g.S;
       if (hp->normuon) {
         MNS_HIP(timed("row_sumsq", 0, sel * es, s, [&] {
-          return row_sumsq_x(O, g.elem, g.n_p, g.m_p, c, g.n, g.m, g.tall, w.part, s); }));
+          return row_sumsq_x(O, g.elem, g.rows_p, g.cols_p, c, k, cols, w.part, s); }));
         MNS_HIP(timed("normuon_finalize", 0, 4.0 * c * k * (w.chunks + 3), s, [&] {
           return normuon_finalize(w.part, w.chunks, c, k, cols, &Vp, nullptr, 0,
                                   dion ? w.S : nullptr, hp->beta2, hp->eps, inv_s * inv_s, inv_s,
@@ -485,7 +510,7 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
           return fill(w.rowscale, (int64_t)c * k, inv_s, s); }));
       }
       MNS_HIP(timed("weight_update", 0, sel * (2.0 * ss + es) + 4.0 * c * k, s, [&] {
-        return weight_update(Wp, sto, c, k, cols, O, g.elem, g.n_p, g.m_p, g.tall, w.rowscale,
+        return weight_update(Wp, sto, c, k, cols, O, g.elem, g.rows_p, g.cols_p, w.rowscale,
                              dion ? w.S : nullptr, k, hp->lr, s); }));
     }
   }
@@ -514,6 +539,8 @@ mns_status mns_ns_workspace_size(int dtype, int64_t batch, int64_t rows, int64_t
   if (st != MNS_OK) return st;
   st = check_shape(batch, rows, cols);
   if (st != MNS_OK) return st;
+  st = check_iterate(rows, cols, dtype == MNS_BF16 ? Store::BF16 : Store::F32);
+  if (st != MNS_OK) return st;
   if (kind != MNS_NS_STANDARD && kind != MNS_NS_GRAM) return MNS_ERR_PARAM;
   const Geo g = make_geo(rows, cols, dtype == MNS_BF16 ? Store::BF16 : Store::F32);
   const int c = batch < kChunk ? (int)batch : kChunk;
@@ -527,6 +554,8 @@ static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch
   mns_status st = check_dtype(dtype);
   if (st != MNS_OK) return st;
   st = check_shape(batch, rows, cols);
+  if (st != MNS_OK) return st;
+  st = check_iterate(rows, cols, dtype == MNS_BF16 ? Store::BF16 : Store::F32);
   if (st != MNS_OK) return st;
   if (!X || !O) return MNS_ERR_NULL;
   st = check_ns(T, abc, kind, restart_mask);
@@ -552,14 +581,14 @@ static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch
       return sumsq(xin, sto, c, rows * cols, partials, s); }));
     MNS_HIP(timed("finalize_scale", 0, 4.0 * c * nblk, s, [&] {
       return finalize_scale(partials, nblk, c, g.S, xscale, s); }));
-    MNS_HIP(timed("normalize", 0, all * (ss + es), s, [&] {
-      return normalize(nullptr, xin, false, sto, c, rows, cols, g.tall, xscale, g.elem, nb.X0,
-                       g.n_p, g.m_p, s); }));
+    MNS_HIP(timed("normalize", 0, all * (ss + 2.0 * es), s, [&] {
+      return normalize(nullptr, xin, false, sto, c, rows, cols, xscale, g.elem, straight(g, nb),
+                       transposed(g, nb), g.rows_p, g.cols_p, s); }));
     void* res = nullptr;
     st = run_ns(g, c, nb, kind, T, abc, restart_mask, s, &res);
     if (st != MNS_OK) return st;
     MNS_HIP(timed("export", 0, all * (ss + es), s, [&] {
-      return export_output(res, g.elem, g.n_p, g.m_p, c, rows, cols, g.tall, 1.0f / g.S, out,
+      return export_output(res, g.elem, g.rows_p, g.cols_p, c, rows, cols, 1.0f / g.S, out,
                            sto, s); }));
   }
   return MNS_OK;
@@ -630,8 +659,8 @@ mns_status normuon_scale(void* O, int dtype, int64_t batch, int64_t rows, int64_
 mns_status mns_profile_begin(void) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (ProfRec& r : g_prof) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
   g_prof_failed = false;
@@ -649,8 +678,8 @@ mns_status mns_profile_end(mns_kernel_stat* out, int capacity, int* count) {
     float ms = 0.f;
     if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
       ok = false;
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
     mns_kernel_stat* st = nullptr;
     for (auto& x : stats)
       if (std::strncmp(x.name, r.name, sizeof(x.name)) == 0) st = &x;

@@ -199,78 +199,69 @@ __global__ __launch_bounds__(kThreads) void k_finalize_scale(const float* partia
   if (threadIdx.x == 0) xscale[b] = s > 0.0 ? (float)((double)S / sqrt(s)) : 0.f;
 }
 
-// ---- a2: X_0 = scale * M into the zero-padded n_p x m_p iterate ---------------------------
+// ---- a2: X_0 = scale * M, in both layouts, zero padded -------------------------------------
 
+// One block per 64 x 64 tile of the padded source: the scaled tile goes to S (same
+// layout as the source, 8-byte row chunks) and, through LDS, to T transposed.
 template <typename TS, typename TX>
-__global__ __launch_bounds__(kThreads) void k_normalize_wide(PtrPack src, const TS* base,
-                                                             int64_t rows, int64_t cols,
-                                                             const float* xscale, TX* X0,
-                                                             int64_t n_p, int64_t m_p) {
+__global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* base, int64_t rows,
+                                                        int64_t cols, const float* xscale, TX* S,
+                                                        TX* T, int64_t rows_p, int64_t cols_p) {
+  __shared__ float tile[64][65];
   const int b = blockIdx.z;
   const TS* s = base ? base + (int64_t)b * rows * cols : static_cast<const TS*>(src.p[b]);
-  TX* x = X0 + (int64_t)b * n_p * m_p;
+  TX* so = S + (int64_t)b * rows_p * cols_p;
+  TX* to = T + (int64_t)b * rows_p * cols_p;
   const float sc = xscale[b];
-  const int64_t c0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
-  if (c0 >= m_p) return;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const bool vec_ok = (cols % 4) == 0;
-  for (int64_t r = blockIdx.y; r < n_p; r += gridDim.y) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = ty + 16 * i;
+    const int64_t r = r0 + lr, c = c0 + 4 * tx;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < rows) {
-      if (vec_ok && c0 + 4 <= cols) {
-        v = load4<TS>(s, r * cols + c0);
+      if (vec_ok && c + 4 <= cols) {
+        v = load4<TS>(s, r * cols + c);
       } else {
-        float t[4];
+        float t4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = (c0 + e < cols) ? load1<TS>(s, r * cols + c0 + e) : 0.f;
-        v = make_float4(t[0], t[1], t[2], t[3]);
+        for (int e = 0; e < 4; ++e) t4[e] = (c + e < cols) ? load1<TS>(s, r * cols + c + e) : 0.f;
+        v = make_float4(t4[0], t4[1], t4[2], t4[3]);
       }
     }
     v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
-    store4<TX>(x, r * m_p + c0, v);
-  }
-}
-
-// Tall source (rows > cols): X_0[a][b] = scale * src[b][a] through a 64 x 64 LDS tile.
-template <typename TS, typename TX>
-__global__ __launch_bounds__(kThreads) void k_normalize_tall(PtrPack src, const TS* base,
-                                                             int64_t rows, int64_t cols,
-                                                             const float* xscale, TX* X0,
-                                                             int64_t n_p, int64_t m_p) {
-  __shared__ float tile[64][65];
-  const int bz = blockIdx.z;
-  const TS* s = base ? base + (int64_t)bz * rows * cols : static_cast<const TS*>(src.p[bz]);
-  TX* x = X0 + (int64_t)bz * n_p * m_p;
-  const float sc = xscale[bz];
-  const int64_t a0 = (int64_t)blockIdx.y * 64;   // X_0 row block (source column)
-  const int64_t b0 = (int64_t)blockIdx.x * 64;   // X_0 column block (source row)
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t br = b0 + ty + 4 * i, ac = a0 + tx;
-    tile[ty + 4 * i][tx] = (br < rows && ac < cols) ? load1<TS>(s, br * cols + ac) * sc : 0.f;
+    store4<TX>(so, r * cols_p + c, v);
+    tile[lr][4 * tx + 0] = v.x;
+    tile[lr][4 * tx + 1] = v.y;
+    tile[lr][4 * tx + 2] = v.z;
+    tile[lr][4 * tx + 3] = v.w;
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t a = a0 + ty + 4 * i, bcol = b0 + tx;
-    store1<TX>(x, a * m_p + bcol, tile[tx][ty + 4 * i]);
+  for (int i = 0; i < 4; ++i) {
+    const int lc = ty + 16 * i;
+    const float4 v = make_float4(tile[4 * tx + 0][lc], tile[4 * tx + 1][lc], tile[4 * tx + 2][lc],
+                                 tile[4 * tx + 3][lc]);
+    store4<TX>(to, (c0 + lc) * rows_p + r0 + 4 * tx, v);
   }
 }
 
-// ---- O (caller layout) = inv_s * iterate ---------------------------------------------------
+// ---- O (caller layout) = inv_s * iterate in the stored layout ------------------------------
 
 template <typename TX, typename TO>
-__global__ __launch_bounds__(kThreads) void k_export_wide(const TX* X, int64_t n_p, int64_t m_p,
-                                                          int64_t rows, int64_t cols, float inv_s,
-                                                          TO* O) {
+__global__ __launch_bounds__(kThreads) void k_export(const TX* X, int64_t rows_p, int64_t cols_p,
+                                                     int64_t rows, int64_t cols, float inv_s,
+                                                     TO* O) {
   const int b = blockIdx.z;
-  const TX* x = X + (int64_t)b * n_p * m_p;
+  const TX* x = X + (int64_t)b * rows_p * cols_p;
   TO* o = O + (int64_t)b * rows * cols;
   const int64_t c0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (c0 >= cols) return;
   const bool vec_ok = (cols % 4) == 0;
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    float4 v = load4<TX>(x, r * m_p + c0);
+    float4 v = load4<TX>(x, r * cols_p + c0);
     v.x *= inv_s; v.y *= inv_s; v.z *= inv_s; v.w *= inv_s;
     if (vec_ok) {
       store4<TO>(o, r * cols + c0, v);
@@ -281,77 +272,27 @@ __global__ __launch_bounds__(kThreads) void k_export_wide(const TX* X, int64_t n
   }
 }
 
-template <typename TX, typename TO>
-__global__ __launch_bounds__(kThreads) void k_export_tall(const TX* X, int64_t n_p, int64_t m_p,
-                                                          int64_t rows, int64_t cols, float inv_s,
-                                                          TO* O) {
-  __shared__ float tile[64][65];
-  const int bz = blockIdx.z;
-  const TX* x = X + (int64_t)bz * n_p * m_p;
-  TO* o = O + (int64_t)bz * rows * cols;
-  const int64_t a0 = (int64_t)blockIdx.y * 64;   // iterate row block = output column block
-  const int64_t b0 = (int64_t)blockIdx.x * 64;   // iterate column block = output row block
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t a = a0 + ty + 4 * i;
-    tile[ty + 4 * i][tx] = load1<TX>(x, a * m_p + b0 + tx);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t r = b0 + ty + 4 * i, c = a0 + tx;
-    if (r < rows && c < cols) store1<TO>(o, r * cols + c, tile[tx][ty + 4 * i] * inv_s);
-  }
-}
-
 // ---- NorMuon statistics: per stored row, partial sums of O^2 -------------------------------
 
-// One block per 256 x 256 tile of the X-layout iterate. Wide: stored rows are iterate rows,
-// partial over the tile's 256 columns -> part[chunk = tile column][row]. Tall: stored rows
-// are iterate columns, partial over the tile's 256 rows -> part[chunk = tile row][column].
+// One block per 256 x 256 tile of the iterate in the stored layout: partial sums of each
+// row's squares over the tile's 256 columns -> part[chunk = tile column][row].
 template <typename TX>
-__global__ __launch_bounds__(kThreads) void k_row_sumsq_x(const TX* X, int64_t n_p, int64_t m_p,
-                                                          int64_t n, int64_t m, int tall,
+__global__ __launch_bounds__(kThreads) void k_row_sumsq_x(const TX* X, int64_t rows_p,
+                                                          int64_t cols_p, int64_t rows,
                                                           float* part) {
-  constexpr int VEC = 4;
-  constexpr int TPR = 256 / VEC;          // threads per 256-wide row segment (64)
-  constexpr int RPI = kThreads / TPR;     // rows per iteration (4)
-  __shared__ float sh[RPI][256];
+  constexpr int TPR = 64;                 // one wave per 256-wide row segment (4 per thread)
+  constexpr int RPI = kThreads / TPR;     // rows per iteration
   const int b = blockIdx.z;
-  const TX* x = X + (int64_t)b * n_p * m_p;
-  const int64_t r0 = (int64_t)blockIdx.y * 256, c0 = (int64_t)blockIdx.x * 256;
-  const int lane_c = threadIdx.x % TPR, rg = threadIdx.x / TPR;
-  const int64_t c = c0 + lane_c * VEC;
-  if (!tall) {
-    const int64_t chunks = m_p / 256;
-    float* out = part + (int64_t)b * chunks * n + (int64_t)blockIdx.x * n;
-    for (int it = 0; it < 256 / RPI; ++it) {
-      const int64_t r = r0 + it * RPI + rg;
-      const float4 v = load4<TX>(x, r * m_p + c);
-      float s = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-      s = wave_sum(s);                      // TPR == 64: one row per wave
-      if (lane_c == 0 && r < n) out[r] = s;
-    }
-  } else {
-    const int64_t chunks = n_p / 256;
-    float* out = part + (int64_t)b * chunks * m + (int64_t)blockIdx.y * m;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int it = 0; it < 256 / RPI; ++it) {
-      const int64_t r = r0 + it * RPI + rg;
-      const float4 v = load4<TX>(x, r * m_p + c);
-      acc.x += v.x * v.x; acc.y += v.y * v.y; acc.z += v.z * v.z; acc.w += v.w * v.w;
-    }
-    sh[rg][lane_c * VEC + 0] = acc.x;
-    sh[rg][lane_c * VEC + 1] = acc.y;
-    sh[rg][lane_c * VEC + 2] = acc.z;
-    sh[rg][lane_c * VEC + 3] = acc.w;
-    __syncthreads();
-    const int col = threadIdx.x;
-    float s = 0.f;
-#pragma unroll
-    for (int g = 0; g < RPI; ++g) s += sh[g][col];
-    if (c0 + col < m) out[c0 + col] = s;
+  const TX* x = X + (int64_t)b * rows_p * cols_p;
+  const int64_t r0 = (int64_t)blockIdx.y * 256, c = (int64_t)blockIdx.x * 256 + (threadIdx.x % TPR) * 4;
+  const int64_t chunks = cols_p / 256;
+  float* out = part + (int64_t)b * chunks * rows + (int64_t)blockIdx.x * rows;
+  for (int it = 0; it < 256 / RPI; ++it) {
+    const int64_t r = r0 + it * RPI + threadIdx.x / TPR;
+    const float4 v = load4<TX>(x, r * cols_p + c);
+    float s = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    s = wave_sum(s);
+    if ((threadIdx.x % TPR) == 0 && r < rows) out[r] = s;
   }
 }
 
@@ -419,14 +360,14 @@ __global__ __launch_bounds__(kThreads) void k_fill(float* p, int64_t n, float va
 // ---- a7: fused weight update W <- W - lr * rowscale_i * O_ij, one rounding ------------------
 
 template <typename TW, typename TX>
-__global__ __launch_bounds__(kThreads) void k_wupdate_wide(PtrPack Wp, int64_t rows, int64_t cols,
-                                                           const TX* X, int64_t n_p, int64_t m_p,
-                                                           const float* rowscale,
-                                                           const int32_t* rowidx,
-                                                           int64_t rowidx_stride, float lr) {
+__global__ __launch_bounds__(kThreads) void k_wupdate(PtrPack Wp, int64_t rows, int64_t cols,
+                                                      const TX* X, int64_t rows_p, int64_t cols_p,
+                                                      const float* rowscale,
+                                                      const int32_t* rowidx,
+                                                      int64_t rowidx_stride, float lr) {
   const int b = blockIdx.z;
   TW* w = static_cast<TW*>(Wp.p[b]);
-  const TX* x = X + (int64_t)b * n_p * m_p;
+  const TX* x = X + (int64_t)b * rows_p * cols_p;
   const float* rs = rowscale + (int64_t)b * rows;
   const int32_t* ri = rowidx ? rowidx + (int64_t)b * rowidx_stride : nullptr;
   const int64_t c0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -435,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void k_wupdate_wide(PtrPack Wp, int64_t r
   for (int64_t p = blockIdx.y; p < rows; p += gridDim.y) {
     const int64_t wr = ri ? (int64_t)ri[p] : p;
     const float k = -lr * rs[p];
-    const float4 o = load4<TX>(x, p * m_p + c0);
+    const float4 o = load4<TX>(x, p * cols_p + c0);
     if (vec_ok) {
       float4 wv = load4<TW>(w, wr * cols + c0);
       wv.x = fmaf(k, o.x, wv.x);
@@ -449,39 +390,6 @@ __global__ __launch_bounds__(kThreads) void k_wupdate_wide(PtrPack Wp, int64_t r
         const int64_t idx = wr * cols + c0 + e;
         store1<TW>(w, idx, fmaf(k, t[e], load1<TW>(w, idx)));
       }
-    }
-  }
-}
-
-// Tall: the update of W[p][j] is the iterate's element [j][p]; 64 x 64 LDS transpose.
-template <typename TW, typename TX>
-__global__ __launch_bounds__(kThreads) void k_wupdate_tall(PtrPack Wp, int64_t rows, int64_t cols,
-                                                           const TX* X, int64_t n_p, int64_t m_p,
-                                                           const float* rowscale,
-                                                           const int32_t* rowidx,
-                                                           int64_t rowidx_stride, float lr) {
-  __shared__ float tile[64][65];
-  const int bz = blockIdx.z;
-  TW* w = static_cast<TW*>(Wp.p[bz]);
-  const TX* x = X + (int64_t)bz * n_p * m_p;
-  const float* rs = rowscale + (int64_t)bz * rows;
-  const int32_t* ri = rowidx ? rowidx + (int64_t)bz * rowidx_stride : nullptr;
-  const int64_t j0 = (int64_t)blockIdx.y * 64;   // W column block = iterate row block
-  const int64_t p0 = (int64_t)blockIdx.x * 64;   // W row block = iterate column block
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t j = j0 + ty + 4 * i;
-    tile[ty + 4 * i][tx] = load1<TX>(x, j * m_p + p0 + tx);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t p = p0 + ty + 4 * i, j = j0 + tx;
-    if (p < rows && j < cols) {
-      const int64_t wr = ri ? (int64_t)ri[p] : p;
-      const int64_t idx = wr * cols + j;
-      store1<TW>(w, idx, fmaf(-lr * rs[p], tile[tx][ty + 4 * i], load1<TW>(w, idx)));
     }
   }
 }
@@ -632,72 +540,60 @@ hipError_t finalize_scale(const float* partials, int nblk, int count, float S, f
 
 template <typename TS, typename TX>
 static void launch_normalize(const PtrPack* pack, const void* base, int count, int64_t rows,
-                             int64_t cols, bool tall, const float* xscale, void* X0, int64_t n_p,
-                             int64_t m_p, hipStream_t s) {
+                             int64_t cols, const float* xscale, void* S, void* T, int64_t rows_p,
+                             int64_t cols_p, hipStream_t s) {
   PtrPack pk = {};
   if (pack) pk = *pack;
-  const TS* bp = static_cast<const TS*>(base);
-  TX* x = static_cast<TX*>(X0);
-  if (!tall) {
-    dim3 grid((unsigned)((m_p / 4 + kThreads - 1) / kThreads), grid_rows(n_p), count);
-    hipLaunchKernelGGL((k_normalize_wide<TS, TX>), grid, dim3(kThreads), 0, s, pk, bp, rows, cols,
-                       xscale, x, n_p, m_p);
-  } else {
-    dim3 grid((unsigned)(m_p / 64), (unsigned)(n_p / 64), count);
-    hipLaunchKernelGGL((k_normalize_tall<TS, TX>), grid, dim3(kThreads), 0, s, pk, bp, rows, cols,
-                       xscale, x, n_p, m_p);
-  }
+  dim3 grid((unsigned)(cols_p / 64), (unsigned)(rows_p / 64), count);
+  hipLaunchKernelGGL((k_normalize<TS, TX>), grid, dim3(kThreads), 0, s, pk,
+                     static_cast<const TS*>(base), rows, cols, xscale, static_cast<TX*>(S),
+                     static_cast<TX*>(T), rows_p, cols_p);
 }
 
 hipError_t normalize(const PtrPack* pack, const void* base, bool src_f32, Store st, int count,
-                     int64_t rows, int64_t cols, bool tall, const float* xscale, Elem e, void* X0,
-                     int64_t n_p, int64_t m_p, hipStream_t s) {
+                     int64_t rows, int64_t cols, const float* xscale, Elem e, void* S, void* T,
+                     int64_t rows_p, int64_t cols_p, hipStream_t s) {
   const bool f32src = src_f32 || st == Store::F32;
   if (e == Elem::F16) {
-    if (f32src) launch_normalize<float, _Float16>(pack, base, count, rows, cols, tall, xscale, X0, n_p, m_p, s);
-    else launch_normalize<uint16_t, _Float16>(pack, base, count, rows, cols, tall, xscale, X0, n_p, m_p, s);
+    if (f32src) launch_normalize<float, _Float16>(pack, base, count, rows, cols, xscale, S, T, rows_p, cols_p, s);
+    else launch_normalize<uint16_t, _Float16>(pack, base, count, rows, cols, xscale, S, T, rows_p, cols_p, s);
   } else {
-    if (f32src) launch_normalize<float, float>(pack, base, count, rows, cols, tall, xscale, X0, n_p, m_p, s);
-    else launch_normalize<uint16_t, float>(pack, base, count, rows, cols, tall, xscale, X0, n_p, m_p, s);
+    if (f32src) launch_normalize<float, float>(pack, base, count, rows, cols, xscale, S, T, rows_p, cols_p, s);
+    else launch_normalize<uint16_t, float>(pack, base, count, rows, cols, xscale, S, T, rows_p, cols_p, s);
   }
   return last();
 }
 
 template <typename TX, typename TO>
-static void launch_export(const void* X, int64_t n_p, int64_t m_p, int count, int64_t rows,
-                          int64_t cols, bool tall, float inv_s, void* O, hipStream_t s) {
-  const TX* x = static_cast<const TX*>(X);
-  TO* o = static_cast<TO*>(O);
-  if (!tall) {
-    dim3 grid((unsigned)((cols + 4 * kThreads - 1) / (4 * kThreads)), grid_rows(rows), count);
-    hipLaunchKernelGGL((k_export_wide<TX, TO>), grid, dim3(kThreads), 0, s, x, n_p, m_p, rows, cols, inv_s, o);
-  } else {
-    dim3 grid((unsigned)(m_p / 64), (unsigned)(n_p / 64), count);
-    hipLaunchKernelGGL((k_export_tall<TX, TO>), grid, dim3(kThreads), 0, s, x, n_p, m_p, rows, cols, inv_s, o);
-  }
+static void launch_export(const void* X, int64_t rows_p, int64_t cols_p, int count, int64_t rows,
+                          int64_t cols, float inv_s, void* O, hipStream_t s) {
+  dim3 grid((unsigned)((cols + 4 * kThreads - 1) / (4 * kThreads)), grid_rows(rows), count);
+  hipLaunchKernelGGL((k_export<TX, TO>), grid, dim3(kThreads), 0, s, static_cast<const TX*>(X),
+                     rows_p, cols_p, rows, cols, inv_s, static_cast<TO*>(O));
 }
 
-hipError_t export_output(const void* X, Elem e, int64_t n_p, int64_t m_p, int count, int64_t rows,
-                         int64_t cols, bool tall, float inv_s, void* O, Store st, hipStream_t s) {
+hipError_t export_output(const void* X, Elem e, int64_t rows_p, int64_t cols_p, int count,
+                         int64_t rows, int64_t cols, float inv_s, void* O, Store st, hipStream_t s) {
   if (e == Elem::F16) {
-    if (st == Store::BF16) launch_export<_Float16, uint16_t>(X, n_p, m_p, count, rows, cols, tall, inv_s, O, s);
-    else launch_export<_Float16, float>(X, n_p, m_p, count, rows, cols, tall, inv_s, O, s);
+    if (st == Store::BF16) launch_export<_Float16, uint16_t>(X, rows_p, cols_p, count, rows, cols, inv_s, O, s);
+    else launch_export<_Float16, float>(X, rows_p, cols_p, count, rows, cols, inv_s, O, s);
   } else {
-    if (st == Store::BF16) launch_export<float, uint16_t>(X, n_p, m_p, count, rows, cols, tall, inv_s, O, s);
-    else launch_export<float, float>(X, n_p, m_p, count, rows, cols, tall, inv_s, O, s);
+    if (st == Store::BF16) launch_export<float, uint16_t>(X, rows_p, cols_p, count, rows, cols, inv_s, O, s);
+    else launch_export<float, float>(X, rows_p, cols_p, count, rows, cols, inv_s, O, s);
   }
   return last();
 }
 
-hipError_t row_sumsq_x(const void* X, Elem e, int64_t n_p, int64_t m_p, int count, int64_t n,
-                       int64_t m, bool tall, float* part, hipStream_t s) {
-  dim3 grid((unsigned)(m_p / 256), (unsigned)(n_p / 256), count);
+hipError_t row_sumsq_x(const void* X, Elem e, int64_t rows_p, int64_t cols_p, int count,
+                       int64_t rows, int64_t cols, float* part, hipStream_t s) {
+  (void)cols;
+  dim3 grid((unsigned)(cols_p / 256), (unsigned)(rows_p / 256), count);
   if (e == Elem::F16)
     hipLaunchKernelGGL(k_row_sumsq_x<_Float16>, grid, dim3(kThreads), 0, s,
-                       static_cast<const _Float16*>(X), n_p, m_p, n, m, tall ? 1 : 0, part);
+                       static_cast<const _Float16*>(X), rows_p, cols_p, rows, part);
   else
     hipLaunchKernelGGL(k_row_sumsq_x<float>, grid, dim3(kThreads), 0, s,
-                       static_cast<const float*>(X), n_p, m_p, n, m, tall ? 1 : 0, part);
+                       static_cast<const float*>(X), rows_p, cols_p, rows, part);
   return last();
 }
 
@@ -734,30 +630,23 @@ hipError_t fill(float* p, int64_t n, float value, hipStream_t s) {
 
 template <typename TW, typename TX>
 static void launch_wupdate(const PtrPack& W, int count, int64_t rows, int64_t cols, const void* X,
-                           int64_t n_p, int64_t m_p, bool tall, const float* rowscale,
+                           int64_t rows_p, int64_t cols_p, const float* rowscale,
                            const int32_t* rowidx, int64_t rowidx_stride, float lr, hipStream_t s) {
-  const TX* x = static_cast<const TX*>(X);
-  if (!tall) {
-    dim3 grid((unsigned)((cols + 4 * kThreads - 1) / (4 * kThreads)), grid_rows(rows), count);
-    hipLaunchKernelGGL((k_wupdate_wide<TW, TX>), grid, dim3(kThreads), 0, s, W, rows, cols, x, n_p,
-                       m_p, rowscale, rowidx, rowidx_stride, lr);
-  } else {
-    dim3 grid((unsigned)(m_p / 64), (unsigned)(n_p / 64), count);
-    hipLaunchKernelGGL((k_wupdate_tall<TW, TX>), grid, dim3(kThreads), 0, s, W, rows, cols, x, n_p,
-                       m_p, rowscale, rowidx, rowidx_stride, lr);
-  }
+  dim3 grid((unsigned)((cols + 4 * kThreads - 1) / (4 * kThreads)), grid_rows(rows), count);
+  hipLaunchKernelGGL((k_wupdate<TW, TX>), grid, dim3(kThreads), 0, s, W, rows, cols,
+                     static_cast<const TX*>(X), rows_p, cols_p, rowscale, rowidx, rowidx_stride, lr);
 }
 
 hipError_t weight_update(const PtrPack& W, Store st, int count, int64_t rows, int64_t cols,
-                         const void* X, Elem e, int64_t n_p, int64_t m_p, bool tall,
+                         const void* X, Elem e, int64_t rows_p, int64_t cols_p,
                          const float* rowscale, const int32_t* rowidx, int64_t rowidx_stride,
                          float lr, hipStream_t s) {
   if (e == Elem::F16) {
-    if (st == Store::BF16) launch_wupdate<uint16_t, _Float16>(W, count, rows, cols, X, n_p, m_p, tall, rowscale, rowidx, rowidx_stride, lr, s);
-    else launch_wupdate<float, _Float16>(W, count, rows, cols, X, n_p, m_p, tall, rowscale, rowidx, rowidx_stride, lr, s);
+    if (st == Store::BF16) launch_wupdate<uint16_t, _Float16>(W, count, rows, cols, X, rows_p, cols_p, rowscale, rowidx, rowidx_stride, lr, s);
+    else launch_wupdate<float, _Float16>(W, count, rows, cols, X, rows_p, cols_p, rowscale, rowidx, rowidx_stride, lr, s);
   } else {
-    if (st == Store::BF16) launch_wupdate<uint16_t, float>(W, count, rows, cols, X, n_p, m_p, tall, rowscale, rowidx, rowidx_stride, lr, s);
-    else launch_wupdate<float, float>(W, count, rows, cols, X, n_p, m_p, tall, rowscale, rowidx, rowidx_stride, lr, s);
+    if (st == Store::BF16) launch_wupdate<uint16_t, float>(W, count, rows, cols, X, rows_p, cols_p, rowscale, rowidx, rowidx_stride, lr, s);
+    else launch_wupdate<float, float>(W, count, rows, cols, X, rows_p, cols_p, rowscale, rowidx, rowidx_stride, lr, s);
   }
   return last();
 }

@@ -31,20 +31,22 @@ constexpr int kPad = 256;
 inline int64_t pad_up(int64_t x) { return (x + kPad - 1) / kPad * kPad; }
 
 // ---------------------------------------------------------------------------------------
-// GEMM (gemm.hip): C = alpha * op(A, B) + beta * D + gamma * I
-//   A: M x K, k-contiguous rows (lda).  B: N x K k-contiguous (b_kmajor) or K x N
-//   n-contiguous.  C, D: M x N row-major.  Batched over blockIdx.z with element strides.
+// GEMM (gemm.hip): C = alpha * A B^T + beta * D + gamma * I
+//   A: M x K, B: N x K, both row-major with k contiguous (lda, ldb). D, C: M x N row-major;
+//   Ct (optional): the same result written transposed (N x M, ldct). Batched over
+//   blockIdx.z with element strides.
 //   sym: M == N, the result is known to be symmetric; only tiles on or above the diagonal
 //   are computed and each is also stored mirrored (within a diagonal tile the upper
-//   triangle is mirrored), so C is exactly symmetric.
-//   M, N, K must be multiples of kPad.
+//   triangle is mirrored), so C is exactly symmetric. Ct must be null.
+//   M, N, K must be multiples of kPad; at least one of C, Ct is given.
 // ---------------------------------------------------------------------------------------
 struct GemmDesc {
   Elem elem = Elem::F16;
   const void* A = nullptr; int64_t lda = 0, sA = 0;
-  const void* B = nullptr; int64_t ldb = 0, sB = 0; bool b_kmajor = true;
-  void* C = nullptr; int64_t ldc = 0, sC = 0;
+  const void* B = nullptr; int64_t ldb = 0, sB = 0;
   const void* D = nullptr; int64_t ldd = 0, sD = 0;
+  void* C = nullptr; int64_t ldc = 0, sC = 0;
+  void* Ct = nullptr; int64_t ldct = 0, sCt = 0;
   int M = 0, N = 0, K = 0, batch = 1;
   float alpha = 1.f, beta = 0.f, gamma = 0.f;
   int diag_limit = 0;          // gamma is added at (i, i) for i < diag_limit
@@ -75,25 +77,25 @@ hipError_t sumsq(const void* X, Store st, int count, int64_t elems, float* parti
 hipError_t finalize_scale(const float* partials, int nblk, int count, float S, float* xscale,
                           hipStream_t s);
 
-// X0 (n_p x m_p, Elem) = xscale * src, zero padded; src is rows x cols (float32 when
-// src_f32, else storage `st`); tall (rows > cols) is written transposed.
-// src pointers: a pack (per matrix) or, when pack == nullptr, base + b * rows * cols.
+// The normalised iterate in both layouts, zero padded: S (rows_p x cols_p) = xscale * src
+// and T (cols_p x rows_p) = its transpose; src is rows x cols (float32 when src_f32, else
+// storage `st`). src pointers: a pack (per matrix) or, when pack == nullptr,
+// base + b * rows * cols. Outputs are batched with stride rows_p * cols_p.
 hipError_t normalize(const PtrPack* pack, const void* base, bool src_f32, Store st, int count,
-                     int64_t rows, int64_t cols, bool tall, const float* xscale, Elem e,
-                     void* X0, int64_t n_p, int64_t m_p, hipStream_t s);
+                     int64_t rows, int64_t cols, const float* xscale, Elem e, void* S, void* T,
+                     int64_t rows_p, int64_t cols_p, hipStream_t s);
 
-// O (rows x cols, storage st) = inv_s * X (Elem, n_p x m_p layout, transposed if tall).
-hipError_t export_output(const void* X, Elem e, int64_t n_p, int64_t m_p, int count,
-                         int64_t rows, int64_t cols, bool tall, float inv_s, void* O, Store st,
+// O (rows x cols, storage st) = inv_s * X, X in the stored layout (rows_p x cols_p, Elem).
+hipError_t export_output(const void* X, Elem e, int64_t rows_p, int64_t cols_p, int count,
+                         int64_t rows, int64_t cols, float inv_s, void* O, Store st,
                          hipStream_t s);
 
-// Per stored row, partial sums of O^2 over 256-wide chunks of the row:
-//   part[b][chunk][row] for the X-layout iterate (n_p x m_p); stored rows are X rows
-//   (wide) or X columns (tall).
-hipError_t row_sumsq_x(const void* X, Elem e, int64_t n_p, int64_t m_p, int count,
-                       int64_t n, int64_t m, bool tall, float* part, hipStream_t s);
+// Per stored row i < rows, partial sums of X^2 over 256-wide column chunks:
+//   part[b][chunk][i], chunk < cols_p / 256, X in the stored layout (rows_p x cols_p).
+hipError_t row_sumsq_x(const void* X, Elem e, int64_t rows_p, int64_t cols_p, int count,
+                       int64_t rows, int64_t cols, float* part, hipStream_t s);
 
-// Same for a caller matrix O (rows x cols, storage st): part[b][chunk][row].
+// Same for a caller matrix O (rows x cols, storage st): part[b][0][row].
 hipError_t row_sumsq_stored(const void* O, Store st, int count, int64_t rows, int64_t cols,
                             float* part, hipStream_t s);
 
@@ -109,10 +111,10 @@ hipError_t normuon_finalize(const float* part, int chunks, int count, int64_t ro
 // rowscale[b][i] = value (plain Muon: every row scaled alike).
 hipError_t fill(float* p, int64_t n, float value, hipStream_t s);
 
-// W[rowidx[i]][j] -= lr * rowscale[i] * O[i][j]  (O from the X-layout iterate, transposed
-// when tall; rowidx null = identity).
+// W[rowidx[i]][j] -= lr * rowscale[i] * X[i][j]  (X in the stored layout, rows_p x cols_p;
+// rowidx null = identity).
 hipError_t weight_update(const PtrPack& W, Store st, int count, int64_t rows, int64_t cols,
-                         const void* X, Elem e, int64_t n_p, int64_t m_p, bool tall,
+                         const void* X, Elem e, int64_t rows_p, int64_t cols_p,
                          const float* rowscale, const int32_t* rowidx, int64_t rowidx_stride,
                          float lr, hipStream_t s);
 
