@@ -42,6 +42,23 @@ def parse():
     return ap.parse_args()
 
 
+def build_inputs(wl, torch, np, synthetic, dev):
+    """The workload's matrices, resident on `dev`: seeded synthetic gradients, zero weights,
+    momenta and second-moment vectors."""
+    W, M, G, V = [], [], [], []
+    for idx, rows, cols in wl.matrices():
+        g = synthetic.gradient(wl.dist, rows, cols, wl.storage, wl.index, 0, idx)
+        if wl.storage == "bf16":
+            G.append(torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).to(dev))
+            W.append(torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev))
+        else:
+            G.append(torch.from_numpy(g).to(dev))
+            W.append(torch.zeros(rows, cols, dtype=torch.float32, device=dev))
+        M.append(torch.zeros(rows, cols, dtype=torch.float32, device=dev))
+        V.append(torch.zeros(rows, dtype=torch.float32, device=dev))
+    return W, M, G, V
+
+
 GEMM_SOURCE = os.path.join(ROOT, "muon_newton_schulz_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 

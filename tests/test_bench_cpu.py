@@ -1,0 +1,47 @@
+"""Host-side checks of bench.py: the one-GPU guard, input construction and the counter lookup
+(no GPU: inputs are built on the CPU)."""
+import dataclasses
+import os
+import subprocess
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synthetic  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_build_inputs_matches_workload():
+    wl = synthetic.CONFIGS[1]
+    W, M, G, V = bench.build_inputs(wl, torch, np, synthetic, torch.device("cpu"))
+    assert len(W) == len(M) == len(G) == len(V) == wl.n_matrices
+    for (idx, r, c), w, m, g, v in zip(wl.matrices(), W, M, G, V):
+        assert w.shape == m.shape == g.shape == (r, c) and v.shape == (r,)
+        assert m.dtype == torch.float32 and not torch.any(m) and not torch.any(w)
+        ref = synthetic.gradient(wl.dist, r, c, wl.storage, wl.index, 0, idx)
+        assert np.array_equal(g.numpy(), ref)
+
+
+def test_build_inputs_bf16_bits_preserved():
+    # a bf16 workload cut to two small matrices: the device copies keep the gradient's bits
+    wl = dataclasses.replace(synthetic.CONFIGS[2], groups=(synthetic.configs.MatrixSpec(64, 192, 2),))
+    W, M, G, V = bench.build_inputs(wl, torch, np, synthetic, torch.device("cpu"))
+    for (idx, r, c), w, g in zip(wl.matrices(), W, G):
+        assert g.dtype == torch.bfloat16 and w.dtype == torch.bfloat16
+        ref = synthetic.gradient(wl.dist, r, c, "bf16", wl.index, 0, idx)
+        assert np.array_equal(g.view(torch.int16).numpy().view(np.uint16), ref.view(np.uint16))
+
+
+def test_traffic_lookup_unknown_kernel_is_none():
+    assert bench.measured_traffic("no_such_kernel", "config2-standard") is None
