@@ -50,6 +50,8 @@ hipError_t timed_gemm(const GemmDesc& d, double flops, hipStream_t s) {
   return timed(gemm_name(d), flops, 0.0, s, [&] { return gemm(d, s); });
 }
 
+
+
 constexpr int64_t kMaxDim = 65536;
 constexpr int64_t kMaxElems = 2147483647LL;
 constexpr int kMaxT = 64;
@@ -110,6 +112,8 @@ struct NsBuffers {
   void* X[2] = {};
   void* Xt[2] = {};
   void* sq[6] = {};        // n_p x n_p scratch: standard uses 2, Gram uses 6
+  float* gemm_scratch = nullptr;
+  size_t gemm_scratch_bytes = 0;
   int64_t x_stride = 0, sq_stride = 0;
 };
 
@@ -123,6 +127,12 @@ void carve_ns(Carver& cv, const Geo& g, int count, int kind, NsBuffers& b) {
   }
   const int nsq = kind == MNS_NS_GRAM ? 6 : 2;
   for (int i = 0; i < nsq; ++i) b.sq[i] = cv.take<char>(es * count * b.sq_stride);
+  // split-k partial sums: at most (output tiles) x (k-tiles / 8) tiles of float32, capped
+  const size_t kparts = (size_t)(g.m_p > g.n_p ? g.m_p : g.n_p) / 256;
+  size_t scratch = (size_t)count * g.n_p * g.n_p * kparts * sizeof(float);
+  if (scratch > kGemmScratchBytes) scratch = kGemmScratchBytes;
+  b.gemm_scratch = cv.take<float>(scratch / sizeof(float));
+  b.gemm_scratch_bytes = scratch;
 }
 
 // Normalisation targets: the stored layout of the source is X for a wide matrix and X^T for
@@ -144,6 +154,7 @@ GemmDesc sym_desc(const Geo& g, int count, const NsBuffers& b, const void* A, co
   d.C = C; d.ldc = g.n_p; d.sC = b.sq_stride;
   d.M = (int)g.n_p; d.N = (int)g.n_p; d.K = K; d.batch = count;
   d.sym = true;
+  d.partial = b.gemm_scratch; d.partial_bytes = b.gemm_scratch_bytes;
   return d;
 }
 
@@ -158,6 +169,7 @@ GemmDesc left_desc(const Geo& g, int count, const NsBuffers& b, const void* L, c
   d.C = C; d.ldc = g.m_p; d.sC = b.x_stride;
   d.Ct = Ct; d.ldct = g.n_p; d.sCt = b.x_stride;
   d.M = (int)g.n_p; d.N = (int)g.m_p; d.K = (int)g.n_p; d.batch = count;
+  d.partial = b.gemm_scratch; d.partial_bytes = b.gemm_scratch_bytes;
   return d;
 }
 

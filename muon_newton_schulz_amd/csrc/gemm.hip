@@ -31,6 +31,11 @@
 //     accumulators hold 4 consecutive output columns of one row.
 //   * The epilogue stages the finished tile in the (then idle) LDS and writes every output
 //     as 16-byte row chunks: [m][n] for C, [n][m] for C^T and for the mirrored tile.
+//   * Work decomposition: whole rounds of tiles (one block per tile, one round = one block
+//     per CU slot); when the last round would be less than half full, its tiles are split
+//     along k so that round is full. Split blocks write float32 partial sums; a second launch
+//     adds each tile's partials in a fixed order and runs the same epilogue (deterministic,
+//     no inter-block waiting).
 #include "mns_internal.h"
 
 #include <type_traits>
@@ -41,6 +46,7 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kChunks = 8;   // 16-byte chunks per LDS row (one 128-byte k-tile)
@@ -111,6 +117,10 @@ struct GemmArgs {
   int diag_limit;
   int tiles_n;      // N / BN (dense grid) or tiles per side (sym)
   int group;        // tile rows per group of the dense tile order
+  int tiles_per_batch;
+  int full_blocks;  // blocks that own a whole tile; tiles beyond are split
+  int split;        // k-parts per split tile
+  float* partial;   // split partial sums, BM*BN floats per (tile, part)
 };
 
 template <typename T>
@@ -127,7 +137,9 @@ __device__ __forceinline__ void load4<float>(const float* p, float* v) {
   v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, bool SYM>
+// FIX = false: the product (whole tiles, and the k-parts of split tiles); FIX = true: one
+// block per split tile adds its partial sums and runs the epilogue.
+template <typename T, int BM, int BN, int WGM, int WGN, bool SYM, bool FIX>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   using Tr = Traits<T>;
   constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -144,14 +156,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // Tile order. Workgroups go round-robin to the 8 XCDs (L2 domains); remap so each XCD
-  // walks a contiguous range of logical tiles, and order those in groups of p.group tile
-  // rows (column-major inside a group), so the CUs of one XCD share A rows and B rows.
-  int t = blockIdx.x;
-  {
-    const int q = (int)gridDim.x / 8;
-    if (t < 8 * q) t = (t % 8) * q + t / 8;
+  // Block -> (tile, k-range, partial slot); see the work decomposition above.
+  // Tile order. Workgroups go round-robin to the 8 XCDs (L2 domains); whole-tile blocks are
+  // remapped so each XCD walks a contiguous range of logical tiles, ordered in groups of
+  // p.group tile rows (column-major inside a group), so the CUs of one XCD share A and B rows.
+  const int KT = p.K / BK;
+  int lin = blockIdx.x, k_begin = 0, k_end = KT, slot = -1;
+  if (FIX) {
+    lin = p.full_blocks + blockIdx.x;
+  } else if (lin < p.full_blocks) {
+    const int q = p.full_blocks / 8;
+    if (lin < 8 * q) lin = (lin % 8) * q + lin / 8;
+  } else {
+    const int r = lin - p.full_blocks, part = r % p.split;
+    lin = p.full_blocks + r / p.split;
+    slot = r;
+    k_begin = (int)((int64_t)part * KT / p.split);
+    k_end = (int)((int64_t)(part + 1) * KT / p.split);
   }
+  // The decode is uniform over the block; state it, so k offsets stay in scalar registers.
+  lin = __builtin_amdgcn_readfirstlane(lin);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  k_begin = __builtin_amdgcn_readfirstlane(k_begin);
+  k_end = __builtin_amdgcn_readfirstlane(k_end);
+  const int64_t bz = lin / p.tiles_per_batch;
+  int t = lin % p.tiles_per_batch;
   int tm, tn;
   if (SYM) {
     tm = 0;
@@ -167,7 +196,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     tn = l / gsize;
   }
   const int m0 = tm * BM, n0 = tn * BN;
-  const int64_t bz = blockIdx.z;
 
   // Buffer resources based at this block's first A row / B row; reads past the batch slice
   // return zero instead of faulting.
@@ -232,17 +260,57 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     }
   };
 
-  const int KT = p.K / BK;     // >= 4: K is a multiple of 256
-  issue(0, 0);
-  block_sync();
-  for (int kt = 0; kt < KT - 1; ++kt) {
-    issue(kt + 1, (kt + 1) & 1);
-    asm volatile("" ::: "memory");
-    compute(kt & 1);
+  // Partial sums of a split tile, in fragment order: the float4 (i, j, g) of thread tid,
+  // acc[i][j][4g .. 4g+3], at ((i * FN + j) * 4 + g) * NT + tid (coalesced both ways).
+  constexpr int TILE_F4 = FM * FN * 4 * NT;
+  if constexpr (!FIX) {
+    const int KL = k_end - k_begin;
+    issue(k_begin, 0);
     block_sync();
+    for (int kl = 0; kl < KL - 1; ++kl) {
+      issue(k_begin + kl + 1, (kl + 1) & 1);
+      asm volatile("" ::: "memory");
+      compute(kl & 1);
+      block_sync();
+    }
+    compute((KL - 1) & 1);
+    if (slot >= 0) {
+      floatx4* P = reinterpret_cast<floatx4*>(p.partial) + (int64_t)slot * TILE_F4;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            floatx4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+            P[((i * FN + j) * 4 + g) * NT + tid] = v;
+          }
+      return;
+    }
+    block_sync();
+  } else {
+    const floatx4* P = reinterpret_cast<const floatx4*>(p.partial) +
+                       (int64_t)blockIdx.x * p.split * TILE_F4;
+    for (int part = 0; part < p.split; ++part, P += TILE_F4) {
+      floatx4 v[FM][FN][4];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) v[i][j][g] = P[((i * FN + j) * 4 + g) * NT + tid];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += v[i][j][g][e];
+    }
   }
-  compute((KT - 1) & 1);
-  block_sync();
 
   // ---- epilogue: v = alpha acc + beta D + gamma I, staged through LDS ----
   // acc[i][j][4g + e] is element (m, n + e) with m = wm*WM + 32i + (lane & 31) and
@@ -351,6 +419,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   }
 }
 
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, bool SYM>
 hipError_t launch(const GemmDesc& d, hipStream_t s) {
   GemmArgs a;
@@ -361,16 +442,37 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   a.alpha = d.alpha; a.beta = d.beta; a.gamma = d.gamma;
   a.diag_limit = d.diag_limit;
   a.group = 4;
-  unsigned tiles;
   if (SYM) {
     const int t = d.M / BM;
     a.tiles_n = t;
-    tiles = (unsigned)(t * (t + 1) / 2);
+    a.tiles_per_batch = t * (t + 1) / 2;
   } else {
     a.tiles_n = d.N / BN;
-    tiles = (unsigned)((d.M / BM) * (d.N / BN));
+    a.tiles_per_batch = (d.M / BM) * (d.N / BN);
   }
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM>), dim3(tiles, 1, d.batch),
+  // Rounds of whole tiles over the CU slots (one 256-tile block per CU, two 128-tile blocks);
+  // a tail round less than half full is split along k (at least 8 k-tiles per part).
+  const int64_t total = (int64_t)a.tiles_per_batch * d.batch;
+  const int slots = cu_count() * (BM >= 256 ? 1 : 2);
+  const int64_t rounds = total / slots, tail = total % slots;
+  const int KT = d.K / Traits<T>::BK;
+  int split = 1;
+  if (tail > 0 && tail <= slots / 2 && d.partial) {
+    int64_t sp = slots / tail;
+    if (sp > KT / 8) sp = KT / 8;
+    const int64_t per = (int64_t)BM * BN * 4;
+    while (sp > 1 && tail * sp * per > (int64_t)d.partial_bytes) --sp;
+    if (sp > 1) split = (int)sp;
+  }
+  a.split = split;
+  a.partial = d.partial;
+  a.full_blocks = (int)(split > 1 ? rounds * slots : total);
+  const unsigned blocks = (unsigned)(a.full_blocks + (split > 1 ? tail * split : 0));
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM, false>), dim3(blocks), dim3(64 * WGM * WGN), 0,
+                     s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || split < 2) return e;
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM, true>), dim3((unsigned)tail),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
@@ -381,12 +483,12 @@ hipError_t dispatch_tile(const GemmDesc& d, hipStream_t s) {
   return launch<T, BT, BT, WGM, WGN, false>(d, s);
 }
 
-// 256 x 256 tiles when they give at least two waves of blocks over the 256 CUs.
+// 256 x 256 tiles when they give at least two rounds of blocks over the CUs, else 128 x 128.
 int tile_for(const GemmDesc& d) {
   if (d.elem == Elem::F32) return 128;
   const int64_t t256 = d.sym ? (int64_t)(d.M / 256) * (d.M / 256 + 1) / 2
                              : (int64_t)(d.M / 256) * (d.N / 256);
-  return t256 * d.batch >= 512 ? 256 : 128;
+  return t256 * d.batch >= 2 * cu_count() ? 256 : 128;
 }
 
 }  // namespace

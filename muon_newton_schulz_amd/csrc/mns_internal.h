@@ -51,7 +51,12 @@ struct GemmDesc {
   float alpha = 1.f, beta = 0.f, gamma = 0.f;
   int diag_limit = 0;          // gamma is added at (i, i) for i < diag_limit
   bool sym = false;
+  float* partial = nullptr;    // scratch for split-k partial sums (may be null: no split)
+  size_t partial_bytes = 0;
 };
+
+// Scratch the GEMM may use for split-k partial sums (part of the caller's workspace).
+constexpr size_t kGemmScratchBytes = size_t(64) << 20;
 hipError_t gemm(const GemmDesc& d, hipStream_t s);
 // Name of the kernel instantiation gemm() launches for this descriptor.
 const char* gemm_name(const GemmDesc& d);

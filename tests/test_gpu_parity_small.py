@@ -53,6 +53,32 @@ def test_ns_quintic(storage, shape):
         assert rel(got[b], want) < TOL[storage]
 
 
+# Work decomposition of the products: 128 x 128 or 256 x 256 output tiles, whole rounds of
+# tiles over the CUs, and a last round that is split along k (partial sums added by a second
+# launch). The comments give the decomposition on a 256-CU device.
+@pytest.mark.parametrize("storage,shape,batch,check", [
+    ("bf16", (256, 4096), 2, (0, 1)),          # X X^T: 6 tiles, k split 8 ways
+    ("f32", (256, 4096), 2, (0, 1)),           # float32 path: k split 16 ways
+    ("bf16", (640, 3000), 1, (0,)),            # ragged padding inside split tiles (6 ways)
+    ("bf16", (3000, 640), 1, (0,)),            # the same, tall
+    ("bf16", (1024, 2048), 16, (0, 9, 15)),    # 576 tiles: one full round, tail split 4 ways
+    ("bf16", (2048, 2048), 15, (0, 14)),       # 256-tiles: two full rounds, tail split 4 ways
+])
+def test_ns_work_decomposition(storage, shape, batch, check):
+    _say("case decomposition", storage, shape, batch)
+    x = _inputs(shape, storage, 8, batch=batch, dist="student_t")
+    X = to_device(x, storage)
+    O = mns.ns_orthogonalize(X, [QUINTIC] * 5)
+    G = mns.gram_ns_orthogonalize(X, [QUINTIC] * 5, restart_before=(3,))
+    torch.cuda.synchronize()
+    got, got_g = to_f64(O), to_f64(G)
+    for b in check:
+        want = oracle.newton_schulz(stored_f64(x[b], storage), [QUINTIC] * 5)
+        assert rel(got[b], want) < TOL[storage], (b, rel(got[b], want))
+        want_g = oracle.gram_newton_schulz(stored_f64(x[b], storage), [QUINTIC] * 5, (3,))
+        assert rel(got_g[b], want_g) < TOL[storage], (b, rel(got_g[b], want_g))
+
+
 @pytest.mark.parametrize("storage", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(300, 900), (900, 300), (512, 512)])
 @pytest.mark.parametrize("restarts", [(), (3,), (2, 4)])
