@@ -14,9 +14,10 @@
  *   - Matrices are dense, row-major, contiguous: element (i, j) of a rows x cols matrix
  *     is at offset i*cols + j; a batch of B such matrices is B consecutive matrices.
  *   - Device pointers must be 16-byte aligned; the workspace must be 256-byte aligned.
- *   - Sizes: 1 <= rows, cols <= 65536 and rows*cols <= 2^31 - 1; the Newton-Schulz iterate,
- *     rows and cols each rounded up to a multiple of 256, must stay below 2 GiB (2 bytes
- *     per element for MNS_BF16, 4 for MNS_F32), else MNS_ERR_SHAPE.
+ *   - Sizes: 1 <= rows, cols <= 65536 and rows*cols <= 2^31 - 1; the Newton-Schulz iterate
+ *     (rows and cols each rounded up to a multiple of 256, and 256 more elements per row,
+ *     in either of its two layouts) must stay below 2 GiB (2 bytes per element for
+ *     MNS_BF16, 4 for MNS_F32), else MNS_ERR_SHAPE.
  *   - Storage dtype (mns_dtype): MNS_BF16 (W, G, X, O stored as bfloat16) or MNS_F32.
  *     Momentum M and NorMuon state v are always float32.
  *   - Ownership: the caller owns every buffer, including the workspace, whose size the

@@ -78,6 +78,7 @@ struct Carver {
 struct Geo {
   int64_t rows, cols, n, m, n_p, m_p;
   int64_t rows_p, cols_p;      // stored layout, padded (the result O is kept this way)
+  int64_t ld_x, ld_t, ld_q;    // row pitch of X (n_p x m_p), X^T (m_p x n_p), n_p x n_p
   bool tall;
   Elem elem;
   float S;
@@ -94,6 +95,9 @@ Geo make_geo(int64_t rows, int64_t cols, Store st) {
   g.m_p = pad_up(g.m);
   g.rows_p = pad_up(rows);
   g.cols_p = pad_up(cols);
+  g.ld_x = padded_ld(g.m_p);
+  g.ld_t = padded_ld(g.n_p);
+  g.ld_q = padded_ld(g.n_p);
   g.elem = st == Store::BF16 ? Elem::F16 : Elem::F32;
   if (g.elem == Elem::F16) {
     int e = (int)std::lround(0.5 * std::log2((double)g.m));
@@ -114,16 +118,17 @@ struct NsBuffers {
   void* sq[6] = {};        // n_p x n_p scratch: standard uses 2, Gram uses 6
   float* gemm_scratch = nullptr;
   size_t gemm_scratch_bytes = 0;
-  int64_t x_stride = 0, sq_stride = 0;
+  int64_t x_stride = 0, xt_stride = 0, sq_stride = 0;   // batch strides (elements)
 };
 
 void carve_ns(Carver& cv, const Geo& g, int count, int kind, NsBuffers& b) {
   const size_t es = (size_t)elem_bytes(g.elem);
-  b.x_stride = g.n_p * g.m_p;
-  b.sq_stride = g.n_p * g.n_p;
+  b.x_stride = g.n_p * g.ld_x;
+  b.xt_stride = g.m_p * g.ld_t;
+  b.sq_stride = g.n_p * g.ld_q;
   for (int i = 0; i < 2; ++i) {
     b.X[i] = cv.take<char>(es * count * b.x_stride);
-    b.Xt[i] = cv.take<char>(es * count * b.x_stride);
+    b.Xt[i] = cv.take<char>(es * count * b.xt_stride);
   }
   const int nsq = kind == MNS_NS_GRAM ? 6 : 2;
   for (int i = 0; i < nsq; ++i) b.sq[i] = cv.take<char>(es * count * b.sq_stride);
@@ -151,7 +156,7 @@ GemmDesc sym_desc(const Geo& g, int count, const NsBuffers& b, const void* A, co
   d.elem = g.elem;
   d.A = A; d.lda = ldab; d.sA = sab;
   d.B = B; d.ldb = ldab; d.sB = sab;
-  d.C = C; d.ldc = g.n_p; d.sC = b.sq_stride;
+  d.C = C; d.ldc = g.ld_q; d.sC = b.sq_stride;
   d.M = (int)g.n_p; d.N = (int)g.n_p; d.K = K; d.batch = count;
   d.sym = true;
   d.partial = b.gemm_scratch; d.partial_bytes = b.gemm_scratch_bytes;
@@ -164,10 +169,10 @@ GemmDesc left_desc(const Geo& g, int count, const NsBuffers& b, const void* L, c
                    void* C, void* Ct) {
   GemmDesc d;
   d.elem = g.elem;
-  d.A = L; d.lda = g.n_p; d.sA = b.sq_stride;
-  d.B = Xt; d.ldb = g.n_p; d.sB = b.x_stride;
-  d.C = C; d.ldc = g.m_p; d.sC = b.x_stride;
-  d.Ct = Ct; d.ldct = g.n_p; d.sCt = b.x_stride;
+  d.A = L; d.lda = g.ld_q; d.sA = b.sq_stride;
+  d.B = Xt; d.ldb = g.ld_t; d.sB = b.xt_stride;
+  d.C = C; d.ldc = g.ld_x; d.sC = b.x_stride;
+  d.Ct = Ct; d.ldct = g.ld_t; d.sCt = b.xt_stride;
   d.M = (int)g.n_p; d.N = (int)g.m_p; d.K = (int)g.n_p; d.batch = count;
   d.partial = b.gemm_scratch; d.partial_bytes = b.gemm_scratch_bytes;
   return d;
@@ -185,16 +190,16 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
   const double nn = (double)count * g.n * g.n;
   for (int t = 0; t < T; ++t) {
     const float a = abc[3 * t], bb = abc[3 * t + 1], c = abc[3 * t + 2];
-    GemmDesc gram = sym_desc(g, count, b, b.X[cur], b.X[cur], g.m_p, b.x_stride, (int)g.m_p, A);
+    GemmDesc gram = sym_desc(g, count, b, b.X[cur], b.X[cur], g.ld_x, b.x_stride, (int)g.m_p, A);
     gram.alpha = inv_s2;
     MNS_HIP(timed_gemm(gram, nn * g.m, s));
     const void* L = A;
     float lalpha = bb;
     if (c != 0.0f) {
-      GemmDesc poly = sym_desc(g, count, b, A, A, g.n_p, b.sq_stride, (int)g.n_p, B);
+      GemmDesc poly = sym_desc(g, count, b, A, A, g.ld_q, b.sq_stride, (int)g.n_p, B);
       poly.alpha = c;
       poly.beta = bb;
-      poly.D = A; poly.ldd = g.n_p; poly.sD = b.sq_stride;
+      poly.D = A; poly.ldd = g.ld_q; poly.sD = b.sq_stride;
       MNS_HIP(timed_gemm(poly, nn * g.n, s));
       L = B;
       lalpha = 1.0f;
@@ -204,7 +209,7 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
                              (!last || g.tall) ? b.Xt[cur ^ 1] : nullptr);
     upd.alpha = lalpha;
     upd.beta = a;
-    upd.D = b.X[cur]; upd.ldd = g.m_p; upd.sD = b.x_stride;   // read in C coordinates
+    upd.D = b.X[cur]; upd.ldd = g.ld_x; upd.sD = b.x_stride;   // read in C coordinates
     MNS_HIP(timed_gemm(upd, 2.0 * nn * g.m, s));
     cur ^= 1;
   }
@@ -228,7 +233,7 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
   const int n = (int)g.n_p;
   const double nn = (double)count * g.n * g.n;
 
-  GemmDesc gram = sym_desc(g, count, b, b.X[cur], b.X[cur], g.m_p, b.x_stride, (int)g.m_p, R);
+  GemmDesc gram = sym_desc(g, count, b, b.X[cur], b.X[cur], g.ld_x, b.x_stride, (int)g.m_p, R);
   gram.alpha = inv_s2;
   MNS_HIP(timed_gemm(gram, nn * g.m, s));
   bool q_identity = true;
@@ -240,28 +245,28 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
                            2.0 * nn * g.m, s));
         cur ^= 1;
       }
-      GemmDesc re = sym_desc(g, count, b, b.X[cur], b.X[cur], g.m_p, b.x_stride, (int)g.m_p, R);
+      GemmDesc re = sym_desc(g, count, b, b.X[cur], b.X[cur], g.ld_x, b.x_stride, (int)g.m_p, R);
       re.alpha = inv_s2;
       MNS_HIP(timed_gemm(re, nn * g.m, s));
       q_identity = true;
     }
-    GemmDesc zd = sym_desc(g, count, b, R, R, g.n_p, b.sq_stride, n, Z);
+    GemmDesc zd = sym_desc(g, count, b, R, R, g.ld_q, b.sq_stride, n, Z);
     zd.alpha = c;
     zd.beta = bb;
-    zd.D = R; zd.ldd = g.n_p; zd.sD = b.sq_stride;
+    zd.D = R; zd.ldd = g.ld_q; zd.sD = b.sq_stride;
     zd.gamma = a;
     zd.diag_limit = (int)g.n;
     MNS_HIP(timed_gemm(zd, nn * g.n, s));
     if (t < T && !((restart_mask >> (t + 1)) & 1u)) {
-      MNS_HIP(timed_gemm(sym_desc(g, count, b, Z, Z, g.n_p, b.sq_stride, n, Z2), nn * g.n, s));
-      MNS_HIP(timed_gemm(sym_desc(g, count, b, R, Z2, g.n_p, b.sq_stride, n, Rt), nn * g.n, s));
+      MNS_HIP(timed_gemm(sym_desc(g, count, b, Z, Z, g.ld_q, b.sq_stride, n, Z2), nn * g.n, s));
+      MNS_HIP(timed_gemm(sym_desc(g, count, b, R, Z2, g.ld_q, b.sq_stride, n, Rt), nn * g.n, s));
       void* tmp = R; R = Rt; Rt = tmp;
     }
     if (q_identity) {
       void* tmp = Q; Q = Z; Z = tmp;
       q_identity = false;
     } else {
-      MNS_HIP(timed_gemm(sym_desc(g, count, b, Q, Z, g.n_p, b.sq_stride, n, Qt), nn * g.n, s));
+      MNS_HIP(timed_gemm(sym_desc(g, count, b, Q, Z, g.ld_q, b.sq_stride, n, Qt), nn * g.n, s));
       void* tmp = Q; Q = Qt; Qt = tmp;
     }
   }
@@ -293,9 +298,12 @@ mns_status check_shape(int64_t batch, int64_t rows, int64_t cols) {
   return MNS_OK;
 }
 
-// The GEMMs address one padded iterate with 32-bit byte offsets.
+// The GEMMs address one padded iterate (either layout, with its row pitch) with 32-bit byte
+// offsets.
 mns_status check_iterate(int64_t rows, int64_t cols, Store st) {
-  const int64_t bytes = pad_up(rows) * pad_up(cols) * (st == Store::BF16 ? 2 : 4);
+  const int64_t rp = pad_up(rows), cp = pad_up(cols);
+  const int64_t a = rp * padded_ld(cp), b = cp * padded_ld(rp);
+  const int64_t bytes = (a > b ? a : b) * (st == Store::BF16 ? 2 : 4);
   return bytes <= kMaxElems ? MNS_OK : MNS_ERR_SHAPE;
 }
 

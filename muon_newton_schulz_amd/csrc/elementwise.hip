@@ -210,8 +210,9 @@ __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* b
   __shared__ float tile[64][65];
   const int b = blockIdx.z;
   const TS* s = base ? base + (int64_t)b * rows * cols : static_cast<const TS*>(src.p[b]);
-  TX* so = S + (int64_t)b * rows_p * cols_p;
-  TX* to = T + (int64_t)b * rows_p * cols_p;
+  const int64_t lds = padded_ld(cols_p), ldt = padded_ld(rows_p);
+  TX* so = S + (int64_t)b * rows_p * lds;
+  TX* to = T + (int64_t)b * cols_p * ldt;
   const float sc = xscale[b];
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* b
       }
     }
     v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
-    store4<TX>(so, r * cols_p + c, v);
+    store4<TX>(so, r * lds + c, v);
     tile[lr][4 * tx + 0] = v.x;
     tile[lr][4 * tx + 1] = v.y;
     tile[lr][4 * tx + 2] = v.z;
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* b
     const int lc = ty + 16 * i;
     const float4 v = make_float4(tile[4 * tx + 0][lc], tile[4 * tx + 1][lc], tile[4 * tx + 2][lc],
                                  tile[4 * tx + 3][lc]);
-    store4<TX>(to, (c0 + lc) * rows_p + r0 + 4 * tx, v);
+    store4<TX>(to, (c0 + lc) * ldt + r0 + 4 * tx, v);
   }
 }
 
@@ -255,13 +256,14 @@ __global__ __launch_bounds__(kThreads) void k_export(const TX* X, int64_t rows_p
                                                      int64_t rows, int64_t cols, float inv_s,
                                                      TO* O) {
   const int b = blockIdx.z;
-  const TX* x = X + (int64_t)b * rows_p * cols_p;
+  const int64_t ldx = padded_ld(cols_p);
+  const TX* x = X + (int64_t)b * rows_p * ldx;
   TO* o = O + (int64_t)b * rows * cols;
   const int64_t c0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (c0 >= cols) return;
   const bool vec_ok = (cols % 4) == 0;
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    float4 v = load4<TX>(x, r * cols_p + c0);
+    float4 v = load4<TX>(x, r * ldx + c0);
     v.x *= inv_s; v.y *= inv_s; v.z *= inv_s; v.w *= inv_s;
     if (vec_ok) {
       store4<TO>(o, r * cols + c0, v);
@@ -283,13 +285,14 @@ __global__ __launch_bounds__(kThreads) void k_row_sumsq_x(const TX* X, int64_t r
   constexpr int TPR = 64;                 // one wave per 256-wide row segment (4 per thread)
   constexpr int RPI = kThreads / TPR;     // rows per iteration
   const int b = blockIdx.z;
-  const TX* x = X + (int64_t)b * rows_p * cols_p;
+  const int64_t ldx = padded_ld(cols_p);
+  const TX* x = X + (int64_t)b * rows_p * ldx;
   const int64_t r0 = (int64_t)blockIdx.y * 256, c = (int64_t)blockIdx.x * 256 + (threadIdx.x % TPR) * 4;
   const int64_t chunks = cols_p / 256;
   float* out = part + (int64_t)b * chunks * rows + (int64_t)blockIdx.x * rows;
   for (int it = 0; it < 256 / RPI; ++it) {
     const int64_t r = r0 + it * RPI + threadIdx.x / TPR;
-    const float4 v = load4<TX>(x, r * cols_p + c);
+    const float4 v = load4<TX>(x, r * ldx + c);
     float s = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     s = wave_sum(s);
     if ((threadIdx.x % TPR) == 0 && r < rows) out[r] = s;
@@ -367,7 +370,8 @@ __global__ __launch_bounds__(kThreads) void k_wupdate(PtrPack Wp, int64_t rows, 
                                                       int64_t rowidx_stride, float lr) {
   const int b = blockIdx.z;
   TW* w = static_cast<TW*>(Wp.p[b]);
-  const TX* x = X + (int64_t)b * rows_p * cols_p;
+  const int64_t ldx = padded_ld(cols_p);
+  const TX* x = X + (int64_t)b * rows_p * ldx;
   const float* rs = rowscale + (int64_t)b * rows;
   const int32_t* ri = rowidx ? rowidx + (int64_t)b * rowidx_stride : nullptr;
   const int64_t c0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void k_wupdate(PtrPack Wp, int64_t rows, 
   for (int64_t p = blockIdx.y; p < rows; p += gridDim.y) {
     const int64_t wr = ri ? (int64_t)ri[p] : p;
     const float k = -lr * rs[p];
-    const float4 o = load4<TX>(x, p * cols_p + c0);
+    const float4 o = load4<TX>(x, p * ldx + c0);
     if (vec_ok) {
       float4 wv = load4<TW>(w, wr * cols + c0);
       wv.x = fmaf(k, o.x, wv.x);

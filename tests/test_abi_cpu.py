@@ -116,6 +116,16 @@ def test_bad_shapes_are_rejected(lib, shape):
     assert _ws_size(lib, [shape])[0] == _abi.MNS_ERR_SHAPE
 
 
+def test_iterate_size_rule_counts_the_row_pitch(lib):
+    # bf16 iterate rows_p x (cols_p + 256) must stay below 2 GiB: 32768 x (32256 + 256) x 2 B
+    # fits, 32768 x (32512 + 256) x 2 B = 2^31 B does not (though rows * cols < 2^31).
+    assert _ws_size(lib, [(32768, 32256)])[0] == 0
+    assert _ws_size(lib, [(32768, 32512)])[0] == _abi.MNS_ERR_SHAPE
+    assert _ws_size(lib, [(32512, 32768)])[0] == _abi.MNS_ERR_SHAPE
+    out = ctypes.c_size_t(0)
+    assert lib.mns_ns_workspace_size(_abi.MNS_BF16, 1, 32768, 32512, 0, ctypes.byref(out)) == _abi.MNS_ERR_SHAPE
+
+
 def test_null_and_misaligned_pointers(lib):
     hp, keep = _hp(normuon=1)
     m = _mats([(64, 128)])
