@@ -33,9 +33,10 @@
 //     as 16-byte row chunks: [m][n] for C, [n][m] for C^T and for the mirrored tile.
 //   * Work decomposition: whole rounds of tiles (one block per tile, one round = one block
 //     per CU slot); when the last round would be less than half full, its tiles are split
-//     along k so that round is full. Split blocks write float32 partial sums; a second launch
-//     adds each tile's partials in a fixed order and runs the same epilogue (deterministic,
-//     no inter-block waiting).
+//     along k so that round is full. Split blocks write float32 partial sums; a later launch
+//     adds each tile's partials in a fixed order (a wide reduction launch first when they
+//     are many) and runs the same epilogue on the sums (deterministic, no inter-block
+//     waiting).
 #include "mns_internal.h"
 
 #include <type_traits>
@@ -121,6 +122,7 @@ struct GemmArgs {
   int full_blocks;  // blocks that own a whole tile; tiles beyond are split
   int split;        // k-parts per split tile
   float* partial;   // split partial sums, BM*BN floats per (tile, part)
+  int fix_parts;    // parts the epilogue launch adds (split, or 1 after k_reduce_parts)
 };
 
 template <typename T>
@@ -138,7 +140,7 @@ __device__ __forceinline__ void load4<float>(const float* p, float* v) {
 }
 
 // FIX = false: the product (whole tiles, and the k-parts of split tiles); FIX = true: one
-// block per split tile adds its partial sums and runs the epilogue.
+// block per split tile sums its partials and runs the epilogue.
 template <typename T, int BM, int BN, int WGM, int WGN, bool SYM, bool FIX>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   using Tr = Traits<T>;
@@ -159,7 +161,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   // Block -> (tile, k-range, partial slot); see the work decomposition above.
   // Tile order. Workgroups go round-robin to the 8 XCDs (L2 domains); whole-tile blocks are
   // remapped so each XCD walks a contiguous range of logical tiles, ordered in groups of
-  // p.group tile rows (column-major inside a group), so the CUs of one XCD share A and B rows.
+  // p.group tile rows (column-major inside a group), so the CUs of one XCD share A and B rows
+  // (dense and symmetric grids alike).
   const int KT = p.K / BK;
   int lin = blockIdx.x, k_begin = 0, k_end = KT, slot = -1;
   if (FIX) {
@@ -183,9 +186,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   int t = lin % p.tiles_per_batch;
   int tm, tn;
   if (SYM) {
-    tm = 0;
-    while (t >= p.tiles_n - tm) { t -= p.tiles_n - tm; ++tm; }
-    tn = tm + t;
+    // Upper-triangle tiles (tm <= tn) in groups of p.group tile rows, column by column
+    // inside a group, like the dense order.
+    const int tt = p.tiles_n;
+    int g0 = 0;
+    tm = tn = 0;
+    for (;;) {
+      const int gs = tt - g0 < p.group ? tt - g0 : p.group;
+      const int cnt = gs * tt - gs * g0 - gs * (gs - 1) / 2;
+      if (t < cnt) {
+        for (int c = g0;; ++c) {
+          const int rows = c - g0 + 1 < gs ? c - g0 + 1 : gs;
+          if (t < rows) { tm = g0 + t; tn = c; break; }
+          t -= rows;
+        }
+        break;
+      }
+      t -= cnt;
+      g0 += gs;
+    }
   } else {
     const int tiles_m = p.M / BM;
     const int per_group = p.group * p.tiles_n;
@@ -291,24 +310,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     }
     block_sync();
   } else {
+    // Sum the tile's first p.fix_parts parts in part order (1 when k_reduce_parts has
+    // already summed all of them into part 0).
     const floatx4* P = reinterpret_cast<const floatx4*>(p.partial) +
                        (int64_t)blockIdx.x * p.split * TILE_F4;
-    for (int part = 0; part < p.split; ++part, P += TILE_F4) {
-      floatx4 v[FM][FN][4];
+    for (int part = 0; part < p.fix_parts; ++part, P += TILE_F4) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) v[i][j][g] = P[((i * FN + j) * 4 + g) * NT + tid];
+          for (int g = 0; g < 4; ++g) {
+            const floatx4 v = P[((i * FN + j) * 4 + g) * NT + tid];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += v[i][j][g][e];
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += v[e];
+          }
     }
   }
 
@@ -419,6 +435,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   }
 }
 
+// Sums the k-parts of every split tile into its part 0, in part order (the same float32
+// additions for every run): one thread per float4, tile_f4 / 256 blocks per tile.
+__global__ __launch_bounds__(256) void k_reduce_parts(floatx4* partial, int split, int tile_f4) {
+  const int chunks = tile_f4 / 256;
+  const int tile = blockIdx.x / chunks, c = blockIdx.x % chunks;
+  floatx4* P = partial + (int64_t)tile * split * tile_f4 + c * 256 + threadIdx.x;
+  floatx4 v = P[0];
+  int part = 1;
+  for (; part + 4 <= split; part += 4) {
+    const floatx4 a = P[(int64_t)part * tile_f4], b = P[(int64_t)(part + 1) * tile_f4];
+    const floatx4 c2 = P[(int64_t)(part + 2) * tile_f4], d = P[(int64_t)(part + 3) * tile_f4];
+    v += a;
+    v += b;
+    v += c2;
+    v += d;
+  }
+  for (; part < split; ++part) v += P[(int64_t)part * tile_f4];
+  P[0] = v;
+}
+
 int cu_count() {
   static int n = 0;
   if (n == 0) {
@@ -466,12 +502,25 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   }
   a.split = split;
   a.partial = d.partial;
+  a.fix_parts = split;
   a.full_blocks = (int)(split > 1 ? rounds * slots : total);
   const unsigned blocks = (unsigned)(a.full_blocks + (split > 1 ? tail * split : 0));
   hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM, false>), dim3(blocks), dim3(64 * WGM * WGN), 0,
                      s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split < 2) return e;
+  // One epilogue block reads all parts of its tile itself when they are few (<= 1 MiB);
+  // more are first summed by a wide reduction launch.
+  constexpr int tile_f4 = BM * BN / 4;
+  static_assert(tile_f4 % 256 == 0, "whole reduce blocks per tile");
+  a.fix_parts = split;
+  if ((int64_t)split * tile_f4 * 16 > (int64_t(1) << 20)) {
+    hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)(tail * (tile_f4 / 256))), dim3(256), 0, s,
+                       reinterpret_cast<floatx4*>(a.partial), split, tile_f4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.fix_parts = 1;
+  }
   hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM, true>), dim3((unsigned)tail),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
