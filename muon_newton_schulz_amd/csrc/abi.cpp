@@ -180,7 +180,7 @@ GemmDesc left_desc(const Geo& g, int count, const NsBuffers& b, const void* L, c
 
 // Standard quintic NS on the normalised iterate (b.X[0], b.Xt[0]) (section "Standard
 // Newton-Schulz"): A = X X^T, B = b A + c A^2, X <- a X + B X. Returns the result in the
-// stored layout (X for a wide matrix, X^T for a tall one; leading dimension cols_p).
+// stored layout (X for a wide matrix, X^T for a tall one; row pitch padded_ld(cols_p)).
 mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, const float* abc,
                         hipStream_t s, void** out) {
   int cur = 0;
@@ -193,23 +193,25 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
     GemmDesc gram = sym_desc(g, count, b, b.X[cur], b.X[cur], g.ld_x, b.x_stride, (int)g.m_p, A);
     gram.alpha = inv_s2;
     MNS_HIP(timed_gemm(gram, nn * g.m, s));
-    const void* L = A;
-    float lalpha = bb;
+    const bool last = t == T - 1;
+    GemmDesc upd = left_desc(g, count, b, A, b.Xt[cur], (!last || !g.tall) ? b.X[cur ^ 1] : nullptr,
+                             (!last || g.tall) ? b.Xt[cur ^ 1] : nullptr);
     if (c != 0.0f) {
+      // P = a I + b A + c A^2 (a on the real diagonal only, so padding stays zero), then
+      // X <- P X: the same map as a X + (b A + c A^2) X, without re-reading X.
       GemmDesc poly = sym_desc(g, count, b, A, A, g.ld_q, b.sq_stride, (int)g.n_p, B);
       poly.alpha = c;
       poly.beta = bb;
       poly.D = A; poly.ldd = g.ld_q; poly.sD = b.sq_stride;
+      poly.gamma = a;
+      poly.diag_limit = (int)g.n;
       MNS_HIP(timed_gemm(poly, nn * g.n, s));
-      L = B;
-      lalpha = 1.0f;
+      upd.A = B;
+    } else {
+      upd.alpha = bb;
+      upd.beta = a;
+      upd.D = b.X[cur]; upd.ldd = g.ld_x; upd.sD = b.x_stride;   // read in C coordinates
     }
-    const bool last = t == T - 1;
-    GemmDesc upd = left_desc(g, count, b, L, b.Xt[cur], (!last || !g.tall) ? b.X[cur ^ 1] : nullptr,
-                             (!last || g.tall) ? b.Xt[cur ^ 1] : nullptr);
-    upd.alpha = lalpha;
-    upd.beta = a;
-    upd.D = b.X[cur]; upd.ldd = g.ld_x; upd.sD = b.x_stride;   // read in C coordinates
     MNS_HIP(timed_gemm(upd, 2.0 * nn * g.m, s));
     cur ^= 1;
   }
