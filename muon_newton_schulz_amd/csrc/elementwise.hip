@@ -84,6 +84,52 @@ __device__ __forceinline__ void store4<_Float16>(_Float16* p, int64_t i, float4 
   *reinterpret_cast<h4*>(p + i) = o;
 }
 
+// 8 consecutive elements (16 bytes of bfloat16/float16, 32 of float32) as two float4.
+struct f8 {
+  float4 lo, hi;
+};
+template <typename TS>
+__device__ __forceinline__ f8 load8(const TS* p, int64_t i) {
+  return {load4<TS>(p, i), load4<TS>(p, i + 4)};
+}
+template <>
+__device__ __forceinline__ f8 load8<uint16_t>(const uint16_t* p, int64_t i) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p + i);
+  return {make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                      bf16_to_f32(v.y >> 16)),
+          make_float4(bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xFFFFu),
+                      bf16_to_f32(v.w >> 16))};
+}
+template <>
+__device__ __forceinline__ f8 load8<_Float16>(const _Float16* p, int64_t i) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const h8 v = *reinterpret_cast<const h8*>(p + i);
+  return {make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]),
+          make_float4((float)v[4], (float)v[5], (float)v[6], (float)v[7])};
+}
+
+template <typename TS>
+__device__ __forceinline__ void store8(TS* p, int64_t i, const f8& v) {
+  store4<TS>(p, i, v.lo);
+  store4<TS>(p, i + 4, v.hi);
+}
+template <>
+__device__ __forceinline__ void store8<uint16_t>(uint16_t* p, int64_t i, const f8& v) {
+  uint4 o;
+  o.x = f32_to_bf16(v.lo.x) | (f32_to_bf16(v.lo.y) << 16);
+  o.y = f32_to_bf16(v.lo.z) | (f32_to_bf16(v.lo.w) << 16);
+  o.z = f32_to_bf16(v.hi.x) | (f32_to_bf16(v.hi.y) << 16);
+  o.w = f32_to_bf16(v.hi.z) | (f32_to_bf16(v.hi.w) << 16);
+  *reinterpret_cast<uint4*>(p + i) = o;
+}
+template <>
+__device__ __forceinline__ void store8<_Float16>(_Float16* p, int64_t i, const f8& v) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const h8 o = {(_Float16)v.lo.x, (_Float16)v.lo.y, (_Float16)v.lo.z, (_Float16)v.lo.w,
+                (_Float16)v.hi.x, (_Float16)v.hi.y, (_Float16)v.hi.z, (_Float16)v.hi.w};
+  *reinterpret_cast<h8*>(p + i) = o;
+}
+
 template <typename TS>
 __device__ __forceinline__ void store1(TS* p, int64_t i, float v);
 template <>
@@ -201,51 +247,66 @@ __global__ __launch_bounds__(kThreads) void k_finalize_scale(const float* partia
 
 // ---- a2: X_0 = scale * M, in both layouts, zero padded -------------------------------------
 
-// One block per 64 x 64 tile of the padded source: the scaled tile goes to S (same
-// layout as the source, 8-byte row chunks) and, through LDS, to T transposed.
+// One block per 64 x 128 tile of the padded source: each thread scales 8 consecutive
+// columns of 4 rows and stores them to S as 16-byte chunks; the tile passes through LDS
+// (float32, padded rows: conflict-free column reads) and leaves transposed to T, again as
+// 16-byte chunks of 8 elements.
+constexpr int kNormRows = 64, kNormCols = 128;
+
 template <typename TS, typename TX>
 __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* base, int64_t rows,
                                                         int64_t cols, const float* xscale, TX* S,
                                                         TX* T, int64_t rows_p, int64_t cols_p) {
-  __shared__ float tile[64][65];
+  __shared__ float tile[kNormRows][kNormCols + 1];
   const int b = blockIdx.z;
   const TS* s = base ? base + (int64_t)b * rows * cols : static_cast<const TS*>(src.p[b]);
   const int64_t lds = padded_ld(cols_p), ldt = padded_ld(rows_p);
   TX* so = S + (int64_t)b * rows_p * lds;
   TX* to = T + (int64_t)b * cols_p * ldt;
   const float sc = xscale[b];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const bool vec_ok = (cols % 4) == 0;
+  const int64_t r0 = (int64_t)blockIdx.y * kNormRows, c0 = (int64_t)blockIdx.x * kNormCols;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;   // 16 x 8 columns, 16 rows per pass
+  const int64_t c = c0 + 8 * tx;
+  const bool vec_ok = (cols % 8) == 0;
+  f8 v[kNormRows / 16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lr = ty + 16 * i;
-    const int64_t r = r0 + lr, c = c0 + 4 * tx;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < kNormRows / 16; ++i) {
+    const int64_t r = r0 + ty + 16 * i;
+    v[i] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
     if (r < rows) {
-      if (vec_ok && c + 4 <= cols) {
-        v = load4<TS>(s, r * cols + c);
+      if (vec_ok && c + 8 <= cols) {
+        v[i] = load8<TS>(s, r * cols + c);
       } else {
-        float t4[4];
+        float t8[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t4[e] = (c + e < cols) ? load1<TS>(s, r * cols + c + e) : 0.f;
-        v = make_float4(t4[0], t4[1], t4[2], t4[3]);
+        for (int e = 0; e < 8; ++e) t8[e] = (c + e < cols) ? load1<TS>(s, r * cols + c + e) : 0.f;
+        v[i] = {make_float4(t8[0], t8[1], t8[2], t8[3]), make_float4(t8[4], t8[5], t8[6], t8[7])};
       }
     }
-    v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
-    store4<TX>(so, r * lds + c, v);
-    tile[lr][4 * tx + 0] = v.x;
-    tile[lr][4 * tx + 1] = v.y;
-    tile[lr][4 * tx + 2] = v.z;
-    tile[lr][4 * tx + 3] = v.w;
+  }
+#pragma unroll
+  for (int i = 0; i < kNormRows / 16; ++i) {
+    const int lr = ty + 16 * i;
+    f8 w = v[i];
+    w.lo.x *= sc; w.lo.y *= sc; w.lo.z *= sc; w.lo.w *= sc;
+    w.hi.x *= sc; w.hi.y *= sc; w.hi.z *= sc; w.hi.w *= sc;
+    store8<TX>(so, (r0 + lr) * lds + c, w);
+    float* t = &tile[lr][8 * tx];
+    t[0] = w.lo.x; t[1] = w.lo.y; t[2] = w.lo.z; t[3] = w.lo.w;
+    t[4] = w.hi.x; t[5] = w.hi.y; t[6] = w.hi.z; t[7] = w.hi.w;
   }
   __syncthreads();
+  // T rows c0 .. c0+127, 64 elements (8 chunks of 8) each: 1024 chunks, 4 per thread
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lc = ty + 16 * i;
-    const float4 v = make_float4(tile[4 * tx + 0][lc], tile[4 * tx + 1][lc], tile[4 * tx + 2][lc],
-                                 tile[4 * tx + 3][lc]);
-    store4<TX>(to, (c0 + lc) * ldt + r0 + 4 * tx, v);
+  for (int i = 0; i < kNormCols * kNormRows / 8 / kThreads; ++i) {
+    const int q = threadIdx.x + kThreads * i;
+    const int lc = q >> 3, ch = q & 7;
+    f8 w;
+    w.lo = make_float4(tile[8 * ch + 0][lc], tile[8 * ch + 1][lc], tile[8 * ch + 2][lc],
+                       tile[8 * ch + 3][lc]);
+    w.hi = make_float4(tile[8 * ch + 4][lc], tile[8 * ch + 5][lc], tile[8 * ch + 6][lc],
+                       tile[8 * ch + 7][lc]);
+    store8<TX>(to, (c0 + lc) * ldt + r0 + 8 * ch, w);
   }
 }
 
@@ -276,25 +337,36 @@ __global__ __launch_bounds__(kThreads) void k_export(const TX* X, int64_t rows_p
 
 // ---- NorMuon statistics: per stored row, partial sums of O^2 -------------------------------
 
-// One block per 256 x 256 tile of the iterate in the stored layout: partial sums of each
-// row's squares over the tile's 256 columns -> part[chunk = tile column][row].
+// One block per 64 x 256 tile of the iterate in the stored layout: partial sums of each
+// row's squares over the tile's 256 columns -> part[chunk = tile column][row]. 32 threads
+// (8 elements each) per row; 8 rows per pass, 8 passes with all loads in flight.
+constexpr int kRsRows = 64;
+
 template <typename TX>
 __global__ __launch_bounds__(kThreads) void k_row_sumsq_x(const TX* X, int64_t rows_p,
                                                           int64_t cols_p, int64_t rows,
                                                           float* part) {
-  constexpr int TPR = 64;                 // one wave per 256-wide row segment (4 per thread)
-  constexpr int RPI = kThreads / TPR;     // rows per iteration
+  constexpr int TPR = 32;                 // threads per 256-wide row chunk
+  constexpr int RPI = kThreads / TPR;     // rows per pass
   const int b = blockIdx.z;
   const int64_t ldx = padded_ld(cols_p);
   const TX* x = X + (int64_t)b * rows_p * ldx;
-  const int64_t r0 = (int64_t)blockIdx.y * 256, c = (int64_t)blockIdx.x * 256 + (threadIdx.x % TPR) * 4;
+  const int64_t r0 = (int64_t)blockIdx.y * kRsRows;
+  const int64_t c = (int64_t)blockIdx.x * 256 + (threadIdx.x % TPR) * 8;
   const int64_t chunks = cols_p / 256;
   float* out = part + (int64_t)b * chunks * rows + (int64_t)blockIdx.x * rows;
-  for (int it = 0; it < 256 / RPI; ++it) {
+  f8 v[kRsRows / RPI];
+#pragma unroll
+  for (int it = 0; it < kRsRows / RPI; ++it)
+    v[it] = load8<TX>(x, (r0 + it * RPI + threadIdx.x / TPR) * ldx + c);
+#pragma unroll
+  for (int it = 0; it < kRsRows / RPI; ++it) {
     const int64_t r = r0 + it * RPI + threadIdx.x / TPR;
-    const float4 v = load4<TX>(x, r * ldx + c);
-    float s = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    s = wave_sum(s);
+    float s = v[it].lo.x * v[it].lo.x + v[it].lo.y * v[it].lo.y + v[it].lo.z * v[it].lo.z +
+              v[it].lo.w * v[it].lo.w + v[it].hi.x * v[it].hi.x + v[it].hi.y * v[it].hi.y +
+              v[it].hi.z * v[it].hi.z + v[it].hi.w * v[it].hi.w;
+#pragma unroll
+    for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_down(s, o, TPR);
     if ((threadIdx.x % TPR) == 0 && r < rows) out[r] = s;
   }
 }
@@ -335,8 +407,14 @@ __global__ __launch_bounds__(kFinThreads) void k_normuon_finalize(
   const float inv_cols = 1.0f / (float)cols;
   double s_o = 0.0, s_h = 0.0;
   for (int64_t i = threadIdx.x; i < rows; i += kFinThreads) {
-    float r = 0.f;
-    for (int c = 0; c < chunks; ++c) r += pt[(int64_t)c * rows + i];
+    float r4[4] = {0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 4 <= chunks; c += 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r4[q] += pt[(int64_t)(c + q) * rows + i];
+    }
+    for (; c < chunks; ++c) r4[0] += pt[(int64_t)c * rows + i];
+    float r = (r4[0] + r4[1]) + (r4[2] + r4[3]);
     r *= inv_s2;
     const int64_t vi = ri ? (int64_t)ri[i] : i;
     const float vn = fmaf(beta2, v[vi], (1.0f - beta2) * (r * inv_cols));
@@ -362,6 +440,9 @@ __global__ __launch_bounds__(kThreads) void k_fill(float* p, int64_t n, float va
 
 // ---- a7: fused weight update W <- W - lr * rowscale_i * O_ij, one rounding ------------------
 
+// Each thread updates 8 consecutive columns of kWuRows rows (all loads issued first).
+constexpr int kWuRows = 4;
+
 template <typename TW, typename TX>
 __global__ __launch_bounds__(kThreads) void k_wupdate(PtrPack Wp, int64_t rows, int64_t cols,
                                                       const TX* X, int64_t rows_p, int64_t cols_p,
@@ -374,25 +455,40 @@ __global__ __launch_bounds__(kThreads) void k_wupdate(PtrPack Wp, int64_t rows, 
   const TX* x = X + (int64_t)b * rows_p * ldx;
   const float* rs = rowscale + (int64_t)b * rows;
   const int32_t* ri = rowidx ? rowidx + (int64_t)b * rowidx_stride : nullptr;
-  const int64_t c0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  const int64_t c0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
   if (c0 >= cols) return;
-  const bool vec_ok = (cols % 4) == 0;
-  for (int64_t p = blockIdx.y; p < rows; p += gridDim.y) {
-    const int64_t wr = ri ? (int64_t)ri[p] : p;
-    const float k = -lr * rs[p];
-    const float4 o = load4<TX>(x, p * ldx + c0);
-    if (vec_ok) {
-      float4 wv = load4<TW>(w, wr * cols + c0);
-      wv.x = fmaf(k, o.x, wv.x);
-      wv.y = fmaf(k, o.y, wv.y);
-      wv.z = fmaf(k, o.z, wv.z);
-      wv.w = fmaf(k, o.w, wv.w);
-      store4<TW>(w, wr * cols + c0, wv);
+  const bool vec_ok = (cols % 8) == 0;
+  for (int64_t p0 = (int64_t)blockIdx.y * kWuRows; p0 < rows; p0 += (int64_t)gridDim.y * kWuRows) {
+    if (vec_ok && p0 + kWuRows <= rows) {
+      f8 o[kWuRows], wv[kWuRows];
+      int64_t wr[kWuRows];
+#pragma unroll
+      for (int q = 0; q < kWuRows; ++q) {
+        wr[q] = ri ? (int64_t)ri[p0 + q] : p0 + q;
+        o[q] = load8<TX>(x, (p0 + q) * ldx + c0);
+        wv[q] = load8<TW>(w, wr[q] * cols + c0);
+      }
+#pragma unroll
+      for (int q = 0; q < kWuRows; ++q) {
+        const float k = -lr * rs[p0 + q];
+        wv[q].lo.x = fmaf(k, o[q].lo.x, wv[q].lo.x);
+        wv[q].lo.y = fmaf(k, o[q].lo.y, wv[q].lo.y);
+        wv[q].lo.z = fmaf(k, o[q].lo.z, wv[q].lo.z);
+        wv[q].lo.w = fmaf(k, o[q].lo.w, wv[q].lo.w);
+        wv[q].hi.x = fmaf(k, o[q].hi.x, wv[q].hi.x);
+        wv[q].hi.y = fmaf(k, o[q].hi.y, wv[q].hi.y);
+        wv[q].hi.z = fmaf(k, o[q].hi.z, wv[q].hi.z);
+        wv[q].hi.w = fmaf(k, o[q].hi.w, wv[q].hi.w);
+        store8<TW>(w, wr[q] * cols + c0, wv[q]);
+      }
     } else {
-      const float t[4] = {o.x, o.y, o.z, o.w};
-      for (int e = 0; e < 4 && c0 + e < cols; ++e) {
-        const int64_t idx = wr * cols + c0 + e;
-        store1<TW>(w, idx, fmaf(k, t[e], load1<TW>(w, idx)));
+      for (int64_t p = p0; p < rows && p < p0 + kWuRows; ++p) {
+        const int64_t r = ri ? (int64_t)ri[p] : p;
+        const float k = -lr * rs[p];
+        for (int e = 0; e < 8 && c0 + e < cols; ++e) {
+          const int64_t idx = r * cols + c0 + e;
+          store1<TW>(w, idx, fmaf(k, load1<TX>(x, p * ldx + c0 + e), load1<TW>(w, idx)));
+        }
       }
     }
   }
@@ -446,33 +542,99 @@ __global__ __launch_bounds__(kThreads) void k_momentum_l1(PtrPack Mp, PtrPack Gp
   }
 }
 
-// rank_i = #{j : l1_j > l1_i or (l1_j == l1_i and j < i)}: a strict total order, so the k
-// rows of rank < k are the top-k with ties resolved towards the lower index. A NaN norm is
-// ordered below every number, which keeps the ranks a permutation (every S slot written).
-constexpr int kTopkChunk = 4096;
+// Top-k rows by l1 norm, ties towards the lower index, by radix selection on an order-
+// preserving 32-bit key (one block per matrix): four 8-bit digit passes find the k-th
+// largest key K and how many rows equal to K still belong to the top k; a compaction then
+// writes the selected rows in ascending index order. A NaN norm is ordered below every
+// number. Integer counts only, so the selection is exact and reproducible.
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
 
-__device__ __forceinline__ float topk_key(float x) { return isnan(x) ? -INFINITY : x; }
+__device__ __forceinline__ uint32_t order_key(float x) {
+  if (isnan(x)) x = -INFINITY;
+  if (x == 0.f) x = 0.f;                       // -0 and +0 are one value
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
-__global__ __launch_bounds__(kThreads) void k_topk(const float* l1, int64_t rows, int64_t k,
-                                                   int32_t* S) {
-  __shared__ float keys[kTopkChunk];
-  const int b = blockIdx.y;
+// Exclusive prefix sum over the block (kSelThreads values), deterministic.
+__device__ int block_exclusive_scan(int v, int* sh) {
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int o = 1; o < kSelThreads; o <<= 1) {
+    const int add = t >= o ? sh[t - o] : 0;
+    __syncthreads();
+    sh[t] += add;
+    __syncthreads();
+  }
+  const int incl = sh[t];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, int64_t rows, int64_t k,
+                                                      int32_t* S) {
+  __shared__ uint32_t hist[kSelWaves][256];
+  __shared__ int scan_sh[kSelThreads];
+  __shared__ uint32_t sh_prefix;
+  __shared__ int64_t sh_remaining;
+  const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
   const float* key = l1 + (int64_t)b * rows;
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const float ki = i < rows ? topk_key(key[i]) : 0.f;
-  int64_t rank = 0;
-  for (int64_t c0 = 0; c0 < rows; c0 += kTopkChunk) {
-    const int64_t len = rows - c0 < kTopkChunk ? rows - c0 : kTopkChunk;
+  uint32_t prefix = 0, mask = 0;
+  int64_t remaining = k;   // rows still to take among those whose key matches prefix on mask
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = t; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
     __syncthreads();
-    for (int64_t t = threadIdx.x; t < len; t += kThreads) keys[t] = topk_key(key[c0 + t]);
+    for (int64_t i = t; i < rows; i += kSelThreads) {
+      const uint32_t u = order_key(key[i]);
+      if ((u & mask) == prefix) atomicAdd(&hist[wave][(u >> shift) & 255u], 1u);
+    }
     __syncthreads();
-    for (int64_t t = 0; t < len; ++t) {
-      const float kj = keys[t];
-      const int64_t j = c0 + t;
-      rank += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
+    if (t < 256) {
+      uint32_t c = 0;
+      for (int w = 0; w < kSelWaves; ++w) c += hist[w][t];
+      hist[0][t] = c;
+    }
+    __syncthreads();
+    if (t == 0) {
+      int64_t above = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (above + (int64_t)hist[0][d] >= remaining) break;
+        above += hist[0][d];
+      }
+      sh_prefix = prefix | ((uint32_t)d << shift);
+      sh_remaining = remaining - above;
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    remaining = sh_remaining;
+    mask |= 255u << shift;
+  }
+  // keys > K are all taken; of the keys == K, the first `remaining` in index order
+  const int64_t per = (rows + kSelThreads - 1) / kSelThreads;
+  const int64_t i0 = (int64_t)t * per, i1 = i0 + per < rows ? i0 + per : rows;
+  int eq = 0;
+  for (int64_t i = i0; i < i1; ++i) eq += order_key(key[i]) == prefix ? 1 : 0;
+  int eq_before = block_exclusive_scan(eq, scan_sh);
+  int sel = 0;
+  {
+    int e = eq_before;
+    for (int64_t i = i0; i < i1; ++i) {
+      const uint32_t u = order_key(key[i]);
+      if (u > prefix) ++sel;
+      else if (u == prefix) sel += (e++ < remaining) ? 1 : 0;
     }
   }
-  if (i < rows && rank < k) S[(int64_t)b * k + rank] = (int32_t)i;
+  int pos = block_exclusive_scan(sel, scan_sh);
+  int e = eq_before;
+  int32_t* out = S + (int64_t)b * k;
+  for (int64_t i = i0; i < i1; ++i) {
+    const uint32_t u = order_key(key[i]);
+    const bool take = u > prefix || (u == prefix && e++ < remaining);
+    if (take) out[pos++] = (int32_t)i;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void k_gather_decay(PtrPack Mp, int64_t cols, int64_t k,
@@ -481,16 +643,36 @@ __global__ __launch_bounds__(kThreads) void k_gather_decay(PtrPack Mp, int64_t c
   __shared__ float sh[kThreads / 64];
   const int b = blockIdx.y;
   float* m = static_cast<float*>(Mp.p[b]);
+  const bool vec_ok = (cols % 4) == 0;
   for (int64_t p = blockIdx.x; p < k; p += gridDim.x) {
     const int64_t src = S[(int64_t)b * k + p];
     float* row = m + src * cols;
     float* dst = Msel + ((int64_t)b * k + p) * cols;
     float acc = 0.f;
-    for (int64_t j = threadIdx.x; j < cols; j += kThreads) {
-      const float v = row[j];
-      dst[j] = v;
-      row[j] = mu * v;
-      acc += v * v;
+    if (vec_ok) {
+      int64_t j = (int64_t)threadIdx.x * 4;
+      for (; j + 4 * kThreads < cols; j += 8 * kThreads) {
+        const float4 v0 = load4<float>(row, j), v1 = load4<float>(row, j + 4 * kThreads);
+        store4<float>(dst, j, v0);
+        store4<float>(dst, j + 4 * kThreads, v1);
+        store4<float>(row, j, make_float4(mu * v0.x, mu * v0.y, mu * v0.z, mu * v0.w));
+        store4<float>(row, j + 4 * kThreads, make_float4(mu * v1.x, mu * v1.y, mu * v1.z, mu * v1.w));
+        acc += v0.x * v0.x + v0.y * v0.y + v0.z * v0.z + v0.w * v0.w;
+        acc += v1.x * v1.x + v1.y * v1.y + v1.z * v1.z + v1.w * v1.w;
+      }
+      if (j < cols) {
+        const float4 v0 = load4<float>(row, j);
+        store4<float>(dst, j, v0);
+        store4<float>(row, j, make_float4(mu * v0.x, mu * v0.y, mu * v0.z, mu * v0.w));
+        acc += v0.x * v0.x + v0.y * v0.y + v0.z * v0.z + v0.w * v0.w;
+      }
+    } else {
+      for (int64_t j = threadIdx.x; j < cols; j += kThreads) {
+        const float v = row[j];
+        dst[j] = v;
+        row[j] = mu * v;
+        acc += v * v;
+      }
     }
     const float s = block_sum<float, kThreads>(acc, sh);
     if (threadIdx.x == 0) partials[(int64_t)b * k + p] = s;
@@ -548,7 +730,7 @@ static void launch_normalize(const PtrPack* pack, const void* base, int count, i
                              int64_t cols_p, hipStream_t s) {
   PtrPack pk = {};
   if (pack) pk = *pack;
-  dim3 grid((unsigned)(cols_p / 64), (unsigned)(rows_p / 64), count);
+  dim3 grid((unsigned)(cols_p / kNormCols), (unsigned)(rows_p / kNormRows), count);
   hipLaunchKernelGGL((k_normalize<TS, TX>), grid, dim3(kThreads), 0, s, pk,
                      static_cast<const TS*>(base), rows, cols, xscale, static_cast<TX*>(S),
                      static_cast<TX*>(T), rows_p, cols_p);
@@ -591,7 +773,7 @@ hipError_t export_output(const void* X, Elem e, int64_t rows_p, int64_t cols_p, 
 hipError_t row_sumsq_x(const void* X, Elem e, int64_t rows_p, int64_t cols_p, int count,
                        int64_t rows, int64_t cols, float* part, hipStream_t s) {
   (void)cols;
-  dim3 grid((unsigned)(cols_p / 256), (unsigned)(rows_p / 256), count);
+  dim3 grid((unsigned)(cols_p / 256), (unsigned)(rows_p / kRsRows), count);
   if (e == Elem::F16)
     hipLaunchKernelGGL(k_row_sumsq_x<_Float16>, grid, dim3(kThreads), 0, s,
                        static_cast<const _Float16*>(X), rows_p, cols_p, rows, part);
@@ -636,7 +818,8 @@ template <typename TW, typename TX>
 static void launch_wupdate(const PtrPack& W, int count, int64_t rows, int64_t cols, const void* X,
                            int64_t rows_p, int64_t cols_p, const float* rowscale,
                            const int32_t* rowidx, int64_t rowidx_stride, float lr, hipStream_t s) {
-  dim3 grid((unsigned)((cols + 4 * kThreads - 1) / (4 * kThreads)), grid_rows(rows), count);
+  dim3 grid((unsigned)((cols + 8 * kThreads - 1) / (8 * kThreads)),
+            grid_rows((rows + kWuRows - 1) / kWuRows), count);
   hipLaunchKernelGGL((k_wupdate<TW, TX>), grid, dim3(kThreads), 0, s, W, rows, cols,
                      static_cast<const TX*>(X), rows_p, cols_p, rowscale, rowidx, rowidx_stride, lr);
 }
@@ -679,8 +862,7 @@ hipError_t momentum_l1(const PtrPack& M, const PtrPack& G, Store g_store, int co
 }
 
 hipError_t topk_rows(const float* l1, int count, int64_t rows, int64_t k, int32_t* S, hipStream_t s) {
-  dim3 grid((unsigned)((rows + kThreads - 1) / kThreads), count);
-  hipLaunchKernelGGL(k_topk, grid, dim3(kThreads), 0, s, l1, rows, k, S);
+  hipLaunchKernelGGL(k_topk, dim3(count), dim3(kSelThreads), 0, s, l1, rows, k, S);
   return last();
 }
 
