@@ -486,10 +486,11 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
     a.tiles_n = d.N / BN;
     a.tiles_per_batch = (d.M / BM) * (d.N / BN);
   }
-  // Rounds of whole tiles over the CU slots (one 256-tile block per CU, two 128-tile blocks);
+  // Rounds of whole tiles over the CU slots (one 256-tile block per CU, two 128-tile blocks,
+  // four 64-tile blocks);
   // a tail round less than half full is split along k (at least 8 k-tiles per part).
   const int64_t total = (int64_t)a.tiles_per_batch * d.batch;
-  const int slots = cu_count() * (BM >= 256 ? 1 : 2);
+  const int slots = cu_count() * (BM >= 256 ? 1 : BM >= 128 ? 2 : 4);
   const int64_t rounds = total / slots, tail = total % slots;
   const int KT = d.K / Traits<T>::BK;
   int split = 1;
@@ -532,12 +533,19 @@ hipError_t dispatch_tile(const GemmDesc& d, hipStream_t s) {
   return launch<T, BT, BT, WGM, WGN, false>(d, s);
 }
 
-// 256 x 256 tiles when they give at least two rounds of blocks over the CUs, else 128 x 128.
+// Tiles per batch entry of a BT x BT grid (upper triangle for sym).
+int64_t tiles_of(const GemmDesc& d, int bt) {
+  const int64_t tm = d.M / bt, tn = d.N / bt;
+  return d.sym ? tm * (tm + 1) / 2 : tm * tn;
+}
+
+// 256 x 256 tiles when they give at least two rounds of blocks over the CUs; 64 x 64 when
+// 128 x 128 tiles would not even fill a quarter of the CUs; else 128 x 128.
 int tile_for(const GemmDesc& d) {
   if (d.elem == Elem::F32) return 128;
-  const int64_t t256 = d.sym ? (int64_t)(d.M / 256) * (d.M / 256 + 1) / 2
-                             : (int64_t)(d.M / 256) * (d.N / 256);
-  return t256 * d.batch >= 2 * cu_count() ? 256 : 128;
+  if (tiles_of(d, 256) * d.batch >= 2 * cu_count()) return 256;
+  if (tiles_of(d, 128) * d.batch * 4 < cu_count()) return 64;
+  return 128;
 }
 
 }  // namespace
@@ -547,15 +555,19 @@ hipError_t gemm(const GemmDesc& d, hipStream_t s) {
   if (d.sym && (d.M != d.N || !d.C || d.Ct)) return hipErrorInvalidValue;
   if (!d.sym && !d.C && !d.Ct) return hipErrorInvalidValue;
   if (d.elem == Elem::F32) return dispatch_tile<float, 128, 2, 2>(d, s);
-  if (tile_for(d) == 256) return dispatch_tile<_Float16, 256, 2, 4>(d, s);
+  const int bt = tile_for(d);
+  if (bt == 256) return dispatch_tile<_Float16, 256, 2, 4>(d, s);
+  if (bt == 64) return dispatch_tile<_Float16, 64, 2, 2>(d, s);
   return dispatch_tile<_Float16, 128, 2, 2>(d, s);
 }
 
 const char* gemm_name(const GemmDesc& d) {
-  const bool f32 = d.elem == Elem::F32;
-  const bool t256 = tile_for(d) == 256;
-  if (d.sym) return f32 ? "gemm_sym_f32_128" : (t256 ? "gemm_sym_f16_256" : "gemm_sym_f16_128");
-  return f32 ? "gemm_nt_f32_128" : (t256 ? "gemm_nt_f16_256" : "gemm_nt_f16_128");
+  if (d.elem == Elem::F32) return d.sym ? "gemm_sym_f32_128" : "gemm_nt_f32_128";
+  switch (tile_for(d)) {
+    case 256: return d.sym ? "gemm_sym_f16_256" : "gemm_nt_f16_256";
+    case 64: return d.sym ? "gemm_sym_f16_64" : "gemm_nt_f16_64";
+    default: return d.sym ? "gemm_sym_f16_128" : "gemm_nt_f16_128";
+  }
 }
 
 }  // namespace mns
