@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -137,6 +139,26 @@ def cpu_baseline(wl, kind, budget_s):
                       f"{len(coeffs)} iterations, fp64 NumPy, {dt:.1f} s"}
 
 
+def graph_timing(mns, torch, step_args, ws, kw, warmup, steps):
+    """The same step recorded once into a HIP graph (torch.cuda.CUDAGraph on the capture
+    stream) and replayed: ms per replayed step."""
+    W, M, G, v = step_args
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        mns.muon_step(W, M, G, v, workspace=ws, stream=torch.cuda.current_stream(), **kw)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"ms_per_step": round(e0.elapsed_time(e1) / steps, 4), "steps": steps}
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -216,6 +238,12 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                 "traffic": measured_traffic(dom["name"], f"config{args.config}-{kind}")}
 
+    graph = None
+    if args.graph:
+        graph = graph_timing(mns, torch, step_args=(W, M, G, v_arg), ws=ws, kw=kw,
+                             warmup=args.warmup, steps=args.steps)
+        graph["eager_ms_per_step"] = round(ms_step, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, kind, args.cpu_seconds)
@@ -242,6 +270,7 @@ def main():
         "mfma_frac_step": round(value / peak, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "graph": graph,
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)

@@ -31,6 +31,12 @@
  *     part of the call's work). No C++ exception crosses this boundary.
  *   - Streams: every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream). Nothing synchronises; the results are ready when the stream reaches them.
+ *   - Graph capture: a call may be recorded into a HIP graph by capturing `stream` (it only
+ *     enqueues kernels: no memset, allocation, synchronisation or host read of device
+ *     data). A replay repeats the call with the pointers, sizes and hyperparameters given
+ *     at capture time. Do not capture while a profiling session is open. The Dion3 page
+ *     (section "3. Dion3 Update Rule", its implementation details) captures the step in a
+ *     graph to remove launch overhead at small scales.
  *   - A zero input matrix yields a zero orthogonalised output (W unchanged), not an error.
  */
 #ifndef MUON_NS_H
