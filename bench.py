@@ -7,7 +7,7 @@ Prints one JSON line: NS algorithmic TFLOP/s over the whole step, step ms, the d
 kernel's roofline (from hipEvents the library records around its launches during the timed
 steps), a per-kernel breakdown, and the fp64 oracle timed on a bounded sample on the host.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {1..5}] [--kind standard|gram]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {1..7}] [--kind standard|gram]
 """
 from __future__ import annotations
 
@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--kind", choices=["standard", "gram"], default=None,
                     help="override the workload's Newton-Schulz variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")

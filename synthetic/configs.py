@@ -8,6 +8,9 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
+# The odd quintic with p(1) = 1, p'(1) = p''(1) = 0: p(x) = (15 x - 10 x^3 + 3 x^5) / 8, whose
+# iteration converges to the polar factor (singular values -> 1) once they are near 1.
+CONVERGENT = (15.0 / 8.0, -10.0 / 8.0, 3.0 / 8.0)
 
 
 @dataclass(frozen=True)
@@ -27,7 +30,7 @@ class Workload:
     mu: float = 0.95
     lr: float = 0.02
     T: int = 5
-    coeffs: tuple = QUINTIC
+    coeffs: tuple = QUINTIC      # one (a, b, c) for every t, or a tuple of T of them
     kind: str = "standard"  # 'standard' or 'gram'
     restart_before: tuple = ()
     normuon: bool = False
@@ -51,6 +54,9 @@ class Workload:
         return out
 
     def coeff_table(self):
+        if isinstance(self.coeffs[0], (tuple, list)):
+            assert len(self.coeffs) == self.T
+            return [tuple(c) for c in self.coeffs]
         return [self.coeffs] * self.T
 
 
@@ -68,4 +74,13 @@ CONFIGS = {
     5: Workload(5, "14B-scale MLP 5120x13824 bf16, Dion3 f=1/4, 10 steps", "bf16",
                 (MatrixSpec(5120, 13824),), "student_t", kind="gram", restart_before=(3,),
                 normuon=True, row_fraction=0.25, lr=0.04, steps=10),
+    # high aspect ratio, as in fine-grained MoE experts: the regime where the Gram
+    # reformulation saves the most (Gram NS + restart vs standard NS: 2.02x fewer FLOPs)
+    6: Workload(6, "MoE experts: 32 x 1024x8192 bf16 (alpha=8)", "bf16",
+                (MatrixSpec(1024, 8192, 32),), "normal", kind="gram", restart_before=(3,),
+                steps=1, extra={"cross_check_standard": True}),
+    # a per-iteration coefficient schedule: four quintic steps, then two convergent ones
+    7: Workload(7, "coefficient schedule: 4 x 2048x8192 bf16, T=6 (4 quintic + 2 convergent)",
+                "bf16", (MatrixSpec(2048, 8192, 4),), "student_t", T=6,
+                coeffs=(QUINTIC,) * 4 + (CONVERGENT,) * 2, steps=1),
 }

@@ -182,3 +182,66 @@ def test_config5_dion3_ten_steps_resynced():
         assert rel(to_f64(V), ref["v"]) < TOL["bf16"], step
         e = check_weight(W1, W0, ref["W_exact"] - W0, "bf16", f"step {step}")
         _say(f"  step {step}: {len(diff)} near-tie swaps, update rel err {e:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_config6_moe_alpha8_gram_and_standard():
+    wl = synthetic.CONFIGS[6]
+    _say("config 6:", wl.name)
+    mats = wl.matrices()
+    G64, Gd = {}, []
+    check = {0, 17, 31}
+    for idx, r, c in mats:
+        g = synthetic.gradient(wl.dist, r, c, "bf16", 6, 0, idx)
+        if idx in check:
+            G64[idx] = stored_f64(g, "bf16")
+        Gd.append(to_device(g, "bf16"))
+    outs = {}
+    for kind in ("gram", "standard"):
+        W = [torch.zeros(r, c, dtype=torch.bfloat16, device="cuda") for _, r, c in mats]
+        M = [torch.zeros(r, c, device="cuda") for _, r, c in mats]
+        mns.muon_step(W, M, Gd, **_kw(wl, kind))
+        torch.cuda.synchronize()
+        outs[kind] = W
+        for idx in sorted(check):
+            _, r, c = mats[idx]
+            _say(f"  {kind} expert {idx}: oracle")
+            ref = oracle.muon_step(np.zeros((r, c)), np.zeros((r, c)), G64[idx], storage="bf16",
+                                   **_oracle_kw(wl, kind))
+            assert rel(to_f64(M[idx]), ref["M"]) < 1e-6
+            e = check_weight(to_f64(W[idx]), 0.0, ref["W_exact"], "bf16", f"{kind} W[{idx}]")
+            _say(f"    update rel err {e:.2e}")
+    # the two algorithms compute the same polynomial map: compare every expert
+    worst = max(rel(to_f64(a), to_f64(b)) for a, b in zip(outs["gram"], outs["standard"]))
+    _say(f"  GPU Gram vs GPU standard, worst of {len(mats)} experts: {worst:.2e}")
+    assert worst < TOL["bf16"]
+
+
+@pytest.mark.timeout(900)
+def test_config7_coefficient_schedule():
+    wl = synthetic.CONFIGS[7]
+    _say("config 7:", wl.name)
+    sched = wl.coeff_table()
+    mats = wl.matrices()
+    G = [synthetic.gradient(wl.dist, r, c, "bf16", 7, 0, idx) for idx, r, c in mats]
+    W = [torch.zeros(r, c, dtype=torch.bfloat16, device="cuda") for _, r, c in mats]
+    M = [torch.zeros(r, c, device="cuda") for _, r, c in mats]
+    mns.muon_step(W, M, [to_device(g, "bf16") for g in G], **_kw(wl))
+    torch.cuda.synchronize()
+    for idx in (0, len(mats) - 1):
+        _, r, c = mats[idx]
+        _say(f"  matrix {idx}: oracle")
+        ref = oracle.muon_step(np.zeros((r, c)), np.zeros((r, c)), stored_f64(G[idx], "bf16"),
+                               storage="bf16", **_oracle_kw(wl))
+        e = check_weight(to_f64(W[idx]), 0.0, ref["W_exact"], "bf16", f"W[{idx}]")
+        _say(f"    update rel err {e:.2e}")
+    # the schedule's two convergent steps land on the polar factor (the plain quintic does
+    # not): the GPU result is within the bf16 gate of U V^T from an fp64 SVD
+    g0 = stored_f64(G[0], "bf16")
+    O = to_f64(mns.ns_orthogonalize(to_device(G[0], "bf16"), sched))
+    Og = to_f64(mns.gram_ns_orthogonalize(to_device(G[0], "bf16"), sched, restart_before=(3,)))
+    torch.cuda.synchronize()
+    polar = oracle.polar_svd(g0)
+    d_std, d_gram = rel(O, polar), rel(Og, polar)
+    _say(f"  GPU standard vs SVD polar {d_std:.2e}; GPU Gram vs SVD polar {d_gram:.2e}")
+    assert d_std < TOL["bf16"] and d_gram < TOL["bf16"]

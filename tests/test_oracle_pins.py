@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import synthetic
 from synthetic import CONFIGS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -145,6 +146,31 @@ def test_singular_values_within_scalar_map_band():
     assert s_out.min() >= band.min() - 1e-12 and s_out.max() <= band.max() + 1e-12
     assert s_out.max() / s_out.min() < 1.7 < s_in.max() / s_in.min()
     assert 0.6 < s_out.min() and s_out.max() < 1.2
+
+
+def test_convergent_quintic_is_second_order_at_one():
+    """The schedule workload's last polynomial, (15 x - 10 x^3 + 3 x^5) / 8, fixes 1 with
+    zero first and second derivative (so iterating it converges to the polar factor)."""
+    a, b, c = synthetic.configs.CONVERGENT
+    assert a + b + c == 1.0
+    assert a + 3 * b + 5 * c == 0.0
+    assert 6 * b + 20 * c == 0.0
+
+
+@pytest.mark.parametrize("shape,seed", [((64, 256), 1), ((128, 512), 2), ((400, 48), 3)])
+def test_coefficient_schedule_reaches_polar(shape, seed):
+    """Four quintic steps then two convergent ones: the closed form with per-iteration
+    coefficients holds, and the output is the polar factor to ~1e-4 (the plain quintic
+    schedule stays ~0.2 away: its fixed point is not 1)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape)
+    sched = CONFIGS[7].coeff_table()
+    out = oracle.newton_schulz(x, sched)
+    assert _rel(out, _closed_form(x, sched)) < 1e-12
+    assert _rel(out, oracle.polar_svd(x)) < 1e-3
+    assert _rel(oracle.newton_schulz(x, [QUINTIC] * 6), oracle.polar_svd(x)) > 0.1
+    s = np.linalg.svd(out, compute_uv=False)
+    assert 0.999 < s.min() and s.max() < 1.0 + 1e-5
 
 
 def test_permutation_equivariance():
