@@ -296,11 +296,12 @@ __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* b
     t[4] = w.hi.x; t[5] = w.hi.y; t[6] = w.hi.z; t[7] = w.hi.w;
   }
   __syncthreads();
-  // T rows c0 .. c0+127, 64 elements (8 chunks of 8) each: 1024 chunks, 4 per thread
+  // T rows c0 .. c0+kNormCols-1, kNormRows elements (chunks of 8) each
+  constexpr int CPT = kNormRows / 8;
 #pragma unroll
   for (int i = 0; i < kNormCols * kNormRows / 8 / kThreads; ++i) {
     const int q = threadIdx.x + kThreads * i;
-    const int lc = q >> 3, ch = q & 7;
+    const int lc = q / CPT, ch = q % CPT;
     f8 w;
     w.lo = make_float4(tile[8 * ch + 0][lc], tile[8 * ch + 1][lc], tile[8 * ch + 2][lc],
                        tile[8 * ch + 3][lc]);

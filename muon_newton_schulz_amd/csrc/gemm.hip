@@ -381,9 +381,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       const int ml = q / CPR_N, c = q % CPR_N;
       const u32x4 v = *reinterpret_cast<const u32x4*>(tile + ml * BN + (c ^ (ml % CPR_N)) * EPC);
       T* dst = Cg + (int64_t)(m0 + ml) * p.ldc + n0 + c * EPC;
-      if (!diag_tile) {
+      // a diagonal tile keeps its upper triangle here: whole chunks right of the diagonal,
+      // element by element in the chunk that holds it, nothing left of it
+      if (!diag_tile || c * EPC >= ml) {
         *reinterpret_cast<u32x4*>(dst) = v;
-      } else {
+      } else if (c * EPC + EPC > ml) {
         const T* vs = reinterpret_cast<const T*>(&v);
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
@@ -423,9 +425,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       const int nl = q / CPR_M, c = q % CPR_M;
       const u32x4 v = *reinterpret_cast<const u32x4*>(tile + nl * BM + c * EPC);
       T* dst = Tg + (int64_t)(n0 + nl) * ldt + m0 + c * EPC;
-      if (!diag_tile) {
+      // a diagonal tile's mirror fills only the strictly lower triangle
+      if (!diag_tile || c * EPC + EPC <= nl) {
         *reinterpret_cast<u32x4*>(dst) = v;
-      } else {
+      } else if (c * EPC < nl) {
         const T* vs = reinterpret_cast<const T*>(&v);
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
