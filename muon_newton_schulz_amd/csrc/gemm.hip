@@ -458,6 +458,135 @@ __global__ __launch_bounds__(256) void k_reduce_parts(floatx4* partial, int spli
   P[0] = v;
 }
 
+// Logical tile `lin` of the grid order -> (tile row, tile column, batch entry); the same
+// order as the product kernel's decode.
+template <bool SYM, int BM>
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int lin, int& tm, int& tn,
+                                            int64_t& bz) {
+  bz = lin / p.tiles_per_batch;
+  int t = lin % p.tiles_per_batch;
+  if (SYM) {
+    // Upper-triangle tiles (tm <= tn) in groups of p.group tile rows, column by column
+    // inside a group, like the dense order.
+    const int tt = p.tiles_n;
+    int g0 = 0;
+    tm = tn = 0;
+    for (;;) {
+      const int gs = tt - g0 < p.group ? tt - g0 : p.group;
+      const int cnt = gs * tt - gs * g0 - gs * (gs - 1) / 2;
+      if (t < cnt) {
+        for (int c = g0;; ++c) {
+          const int rows = c - g0 + 1 < gs ? c - g0 + 1 : gs;
+          if (t < rows) { tm = g0 + t; tn = c; break; }
+          t -= rows;
+        }
+        break;
+      }
+      t -= cnt;
+      g0 += gs;
+    }
+  } else {
+    const int tiles_m = p.M / BM;
+    const int per_group = p.group * p.tiles_n;
+    const int g = t / per_group, l = t % per_group;
+    const int first = g * p.group;
+    const int gsize = tiles_m - first < p.group ? tiles_m - first : p.group;
+    tm = first + l % gsize;
+    tn = l / gsize;
+  }
+}
+
+// Epilogue of the split tail tiles on 64 x 64 sub-tiles (BM/64 x BN/64 blocks of 256 threads
+// per tile): each thread sums four float4 of partial sums (the product kernel's fragment
+// order, p.fix_parts parts in part order), applies alpha, beta D and gamma I, and the sub-tile
+// leaves through LDS as 16-byte rows of C and, transposed, of C^T or of the mirrored tile.
+// Spreading a tile over many CUs keeps the tail's epilogue from running on only a few.
+template <typename T, int BM, int BN, int WGM, int WGN, bool SYM>
+__global__ __launch_bounds__(256) void k_tail_epilogue(GemmArgs p) {
+  constexpr int NT = 64 * WGM * WGN;          // threads of the product kernel
+  constexpr int WM = BM / WGM, WN = BN / WGN, FN = WN / 32;
+  constexpr int ES = (int)sizeof(T), EPC = 16 / ES, SUB = 64, CPR = SUB / EPC;
+  constexpr int TILE_F4 = BM * BN / 4;
+  constexpr int SUBS_N = BN / SUB, SUBS = (BM / SUB) * SUBS_N;
+  static_assert(BM % SUB == 0 && BN % SUB == 0, "whole sub-tiles");
+  typedef T t4 __attribute__((ext_vector_type(4)));
+  typedef T tv __attribute__((ext_vector_type(EPC)));   // one 16-byte chunk
+  __shared__ __align__(16) T tile[SUB][SUB + EPC];
+  const int ti = blockIdx.x / SUBS, sub = blockIdx.x % SUBS;
+  const int sm = (sub / SUBS_N) * SUB, sn = (sub % SUBS_N) * SUB;
+  int tm, tn;
+  int64_t bz;
+  tile_coords<SYM, BM>(p, p.full_blocks + ti, tm, tn, bz);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const floatx4* P = reinterpret_cast<const floatx4*>(p.partial) + (int64_t)ti * p.split * TILE_F4;
+  const T* Dg = p.D ? static_cast<const T*>(p.D) + bz * p.sD : nullptr;
+  // element (ml, nl .. nl+3) of the tile is float4 ((i FN + j) 4 + g) NT + ftid of a part
+  const int ml = sm + (threadIdx.x & 63);
+  const int wm = ml / WM, i = (ml % WM) / 32, lo = ml % 32;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int nl = sn + 4 * ((threadIdx.x >> 6) + 4 * k);
+    const int wn = nl / WN, j = (nl % WN) / 32, g = (nl % 32) / 8, hi = (nl % 8) / 4;
+    const int64_t idx = ((int64_t)(i * FN + j) * 4 + g) * NT + (wm * WGN + wn) * 64 + hi * 32 + lo;
+    floatx4 acc = P[idx];
+    for (int part = 1; part < p.fix_parts; ++part) acc += P[(int64_t)part * TILE_F4 + idx];
+    float d[4] = {0.f, 0.f, 0.f, 0.f};
+    if (Dg) load4<T>(Dg + (int64_t)(m0 + ml) * p.ldd + n0 + nl, d);
+    t4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = p.alpha * acc[e] + p.beta * d[e];
+      if (m0 + ml == n0 + nl + e && m0 + ml < p.diag_limit) v += p.gamma;
+      o[e] = (T)v;
+    }
+    *reinterpret_cast<t4*>(&tile[ml - sm][nl - sn]) = o;
+  }
+  __syncthreads();
+  const bool diag_tile = SYM && tm == tn;
+  if (SYM || p.C) {
+    T* Cg = static_cast<T*>(p.C) + bz * p.sC;
+    for (int q = threadIdx.x; q < SUB * CPR; q += 256) {
+      const int r = q / CPR, c = q % CPR;
+      const int gm = sm + r, gn = sn + c * EPC;
+      const tv v = *reinterpret_cast<const tv*>(&tile[r][c * EPC]);
+      T* dst = Cg + (int64_t)(m0 + gm) * p.ldc + n0 + gn;
+      if (!diag_tile || gn >= gm) {
+        *reinterpret_cast<tv*>(dst) = v;
+      } else if (gn + EPC > gm) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          if (gm <= gn + e) dst[e] = v[e];
+      }
+    }
+  }
+  if (SYM || p.Ct) {
+    T* Tg;
+    int64_t ldt;
+    if (SYM) {
+      Tg = static_cast<T*>(p.C) + bz * p.sC;
+      ldt = p.ldc;
+    } else {
+      Tg = static_cast<T*>(p.Ct) + bz * p.sCt;
+      ldt = p.ldct;
+    }
+    for (int q = threadIdx.x; q < SUB * CPR; q += 256) {
+      const int r = q / CPR, c = q % CPR;       // output row: tile column sn + r
+      const int gn = sn + r, gm = sm + c * EPC;
+      tv vs;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) vs[e] = tile[c * EPC + e][r];
+      T* dst = Tg + (int64_t)(n0 + gn) * ldt + m0 + gm;
+      if (!diag_tile || gm + EPC <= gn) {
+        *reinterpret_cast<tv*>(dst) = vs;
+      } else if (gm < gn) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          if (gm + e < gn) dst[e] = vs[e];
+      }
+    }
+  }
+}
+
 int cu_count() {
   static int n = 0;
   if (n == 0) {
@@ -513,8 +642,8 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
                      s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split < 2) return e;
-  // One epilogue block reads all parts of its tile itself when they are few (<= 1 MiB);
-  // more are first summed by a wide reduction launch.
+  // The tail epilogue reads all parts of a tile itself when they are few (<= 1 MiB per
+  // tile); more are first summed by a wide reduction launch.
   constexpr int tile_f4 = BM * BN / 4;
   static_assert(tile_f4 % 256 == 0, "whole reduce blocks per tile");
   a.fix_parts = split;
@@ -525,8 +654,8 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
     if (e != hipSuccess) return e;
     a.fix_parts = 1;
   }
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM, true>), dim3((unsigned)tail),
-                     dim3(64 * WGM * WGN), 0, s, a);
+  hipLaunchKernelGGL((k_tail_epilogue<T, BM, BN, WGM, WGN, SYM>),
+                     dim3((unsigned)(tail * (BM / 64) * (BN / 64))), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
