@@ -22,11 +22,17 @@
 //     MFMA fragments (v_mfma_f32_32x32x16_f16, or 32x32x2f32 for float32).
 //   * k-tile = 128 bytes per row (64 halves / 32 floats). Both operand tiles sit in LDS as
 //     [row][k] in 16-byte chunks, double buffered, with chunk c of row r stored at
-//     c ^ ((r ^ (r >> 3)) & 7), so a fragment read (32 rows, one chunk) is conflict-free.
+//     c ^ ((r ^ ((r >> 3) & 3)) & 7): a fragment read (32 rows, one chunk) is conflict-free,
+//     and rows 32 apart share the pattern, so the fragments of one k-step sit at fixed
+//     offsets from one address.
 //   * Global -> LDS is a buffer load with the LDS-DMA bit (buffer_load_dwordx4 ... lds):
 //     no staging registers and no LDS store instructions. Each wave instruction fills
-//     1 KB = 8 LDS rows; the lane -> global chunk mapping applies the swizzle. The load of
-//     tile k+1 is in flight while tile k feeds the MFMAs; one barrier per k-tile.
+//     1 KB = 8 LDS rows; the lane -> global chunk mapping applies the swizzle.
+//   * Pipeline (k-step = 16 halves / 4 floats of k, four per k-tile): fragments are read one
+//     k-step ahead of the MFMAs that use them. The barrier of k-tile k comes before its last
+//     k-step, whose fragments are already in registers, so buffer k % 2 is free at that
+//     point and the load of k-tile k+2 goes into it: two k-tiles are in flight with two
+//     buffers, one barrier per k-tile.
 //   * MFMA operand roles are swapped (the B tile feeds the MFMA's A input), so each lane's
 //     accumulators hold 4 consecutive output columns of one row.
 //   * The epilogue stages the finished tile in the (then idle) LDS and writes every output
@@ -81,7 +87,7 @@ struct Traits<float> {
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kChunks + (chunk ^ ((row ^ (row >> 3)) & 7));
+  return row * kChunks + (chunk ^ ((row ^ ((row >> 3) & 3)) & 7));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -139,9 +145,9 @@ __device__ __forceinline__ void load4<float>(const float* p, float* v) {
   v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
 }
 
-// FIX = false: the product (whole tiles, and the k-parts of split tiles); FIX = true: one
-// block per split tile sums its partials and runs the epilogue.
-template <typename T, int BM, int BN, int WGM, int WGN, bool SYM, bool FIX>
+// The product: whole tiles with their epilogue, and the k-parts of split tiles (float32
+// partial sums, finished by k_tail_epilogue).
+template <typename T, int BM, int BN, int WGM, int WGN, bool SYM>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   using Tr = Traits<T>;
   constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -155,7 +161,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
 
   __shared__ u32x4 lds[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS-DMA bases stay scalar
   const int wm = wave / WGN, wn = wave % WGN;
 
   // Block -> (tile, k-range, partial slot); see the work decomposition above.
@@ -165,9 +172,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   // (dense and symmetric grids alike).
   const int KT = p.K / BK;
   int lin = blockIdx.x, k_begin = 0, k_end = KT, slot = -1;
-  if (FIX) {
-    lin = p.full_blocks + blockIdx.x;
-  } else if (lin < p.full_blocks) {
+  if (lin < p.full_blocks) {
     const int q = p.full_blocks / 8;
     if (lin < 8 * q) lin = (lin % 8) * q + lin / 8;
   } else {
@@ -229,13 +234,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < A_INST; ++i) {
     const int row = (wave * A_INST + i) * 8 + (lane >> 3);
-    const int ch = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const int ch = (lane & 7) ^ ((row ^ ((row >> 3) & 3)) & 7);
     offA[i] = (row * (int)p.lda + ch * VEC) * ES;
   }
 #pragma unroll
   for (int i = 0; i < B_INST; ++i) {
     const int row = (wave * B_INST + i) * 8 + (lane >> 3);
-    const int ch = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const int ch = (lane & 7) ^ ((row ^ ((row >> 3) & 3)) & 7);
     offB[i] = (row * (int)p.ldb + ch * VEC) * ES;
   }
 
@@ -267,32 +272,42 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) bf[slot][j] = lds[buf * STAGE + swz(brow + 32 * j, ch)];
   };
-  auto compute = [&](int buf) {
-    load_frags(buf, 0, 0);
+  auto mma_step = [&](int s) {
 #pragma unroll
-    for (int ks = 0; ks < kChunks / 2; ++ks) {
-      if (ks + 1 < kChunks / 2) load_frags(buf, ks + 1, (ks + 1) & 1);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Tr::mma(acc[i][j], bf[ks & 1][j], af[ks & 1][i]);
-    }
+      for (int j = 0; j < FN; ++j) Tr::mma(acc[i][j], bf[s][j], af[s][i]);
   };
 
   // Partial sums of a split tile, in fragment order: the float4 (i, j, g) of thread tid,
   // acc[i][j][4g .. 4g+3], at ((i * FN + j) * 4 + g) * NT + tid (coalesced both ways).
   constexpr int TILE_F4 = FM * FN * 4 * NT;
-  if constexpr (!FIX) {
+  {
+    // The scheduling fences keep each k-step's order as written: the next k-step's LDS reads
+    // go out before this k-step's MFMAs, which then cover their latency.
+    constexpr int KS = kChunks / 2;
     const int KL = k_end - k_begin;
     issue(k_begin, 0);
+    if (KL > 1) issue(k_begin + 1, 1);
     block_sync();
-    for (int kl = 0; kl < KL - 1; ++kl) {
-      issue(k_begin + kl + 1, (kl + 1) & 1);
-      asm volatile("" ::: "memory");
-      compute(kl & 1);
+    load_frags(0, 0, 0);
+    for (int kl = 0; kl < KL; ++kl) {
+      const int b = kl & 1;
+#pragma unroll
+      for (int ks = 0; ks < KS - 1; ++ks) {
+        load_frags(b, ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(ks & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // k-tile kl+1 has landed and every wave's reads of buffer b are done.
       block_sync();
+      if (kl + 2 < KL) issue(k_begin + kl + 2, b);
+      load_frags(b ^ 1, 0, 0);   // after the last k-tile: a harmless read of the idle buffer
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step((KS - 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    compute((KL - 1) & 1);
     if (slot >= 0) {
       floatx4* P = reinterpret_cast<floatx4*>(p.partial) + (int64_t)slot * TILE_F4;
 #pragma unroll
@@ -309,23 +324,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       return;
     }
     block_sync();
-  } else {
-    // Sum the tile's first p.fix_parts parts in part order (1 when k_reduce_parts has
-    // already summed all of them into part 0).
-    const floatx4* P = reinterpret_cast<const floatx4*>(p.partial) +
-                       (int64_t)blockIdx.x * p.split * TILE_F4;
-    for (int part = 0; part < p.fix_parts; ++part, P += TILE_F4) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const floatx4 v = P[((i * FN + j) * 4 + g) * NT + tid];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += v[e];
-          }
-    }
   }
 
   // ---- epilogue: v = alpha acc + beta D + gamma I, staged through LDS ----
@@ -638,7 +636,7 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   a.fix_parts = split;
   a.full_blocks = (int)(split > 1 ? rounds * slots : total);
   const unsigned blocks = (unsigned)(a.full_blocks + (split > 1 ? tail * split : 0));
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM, false>), dim3(blocks), dim3(64 * WGM * WGN), 0,
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM>), dim3(blocks), dim3(64 * WGM * WGN), 0,
                      s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split < 2) return e;
