@@ -31,8 +31,10 @@
 //   * Pipeline (k-step = 16 halves / 4 floats of k, four per k-tile): fragments are read one
 //     k-step ahead of the MFMAs that use them. The barrier of k-tile k comes before its last
 //     k-step, whose fragments are already in registers, so buffer k % 2 is free at that
-//     point and the load of k-tile k+2 goes into it: two k-tiles are in flight with two
-//     buffers, one barrier per k-tile.
+//     point and the load of k-tile k+2 starts into it: two k-tiles are in flight with two
+//     buffers, one barrier per k-tile. Each wave's share of a k-tile load (8 DMA
+//     instructions at 256x256) goes out in three parts, one instruction every few MFMAs,
+//     over the last k-step of k-tile k and the first two of k-tile k+1.
 //   * MFMA operand roles are swapped (the B tile feeds the MFMA's A input), so each lane's
 //     accumulators hold 4 consecutive output columns of one row.
 //   * The epilogue stages the finished tile in the (then idle) LDS and writes every output
@@ -272,42 +274,104 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) bf[slot][j] = lds[buf * STAGE + swz(brow + 32 * j, ch)];
   };
-  auto mma_step = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) Tr::mma(acc[i][j], bf[s][j], af[s][i]);
-  };
 
   // Partial sums of a split tile, in fragment order: the float4 (i, j, g) of thread tid,
   // acc[i][j][4g .. 4g+3], at ((i * FN + j) * 4 + g) * NT + tid (coalesced both ways).
   constexpr int TILE_F4 = FM * FN * 4 * NT;
   {
     // The scheduling fences keep each k-step's order as written: the next k-step's LDS reads
-    // go out before this k-step's MFMAs, which then cover their latency.
+    // go out before this k-step's MFMAs, which then cover their latency, and a k-tile's DMA
+    // instructions go out one at a time between MFMAs (a burst of them fills the vector
+    // memory queue and stalls the waves that issued it).
     constexpr int KS = kChunks / 2;
+    static_assert(KS == 4, "four k-steps per k-tile");
     const int KL = k_end - k_begin;
-    issue(k_begin, 0);
-    if (KL > 1) issue(k_begin + 1, 1);
-    block_sync();
-    load_frags(0, 0, 0);
-    for (int kl = 0; kl < KL; ++kl) {
-      const int b = kl & 1;
+    // DMA instruction q of a k-tile (q < A_INST: A row block q, else B row block q - A_INST).
+    constexpr int NI = A_INST + B_INST;
+    constexpr int NP0 = (NI + 2) / 3, NP1 = (NI + 1) / 3, NP2 = NI / 3;
+    auto dma_one = [&](int kt, int buf, int q) {
+      const int so = kt * BK * ES;
+      if (q < A_INST)
+        dma16(rA, &lds[buf * STAGE + (wave * A_INST + q) * 8 * kChunks], offA[q], so);
+      else
+        dma16(rB, &lds[buf * STAGE + (BM + (wave * B_INST + q - A_INST) * 8) * kChunks],
+              offB[q - A_INST], so);
+    };
+    // One k-step: the MFMAs of fragment slot s with DMA instructions q0 .. q0+nq-1 of k-tile
+    // kt spread between them (after every RR-th MFMA).
+    auto kstep = [&](int s, int kt, int buf, int q0, auto nq_c) {
+      constexpr int NQ = decltype(nq_c)::value;
+      constexpr int NM = FM * FN;
+      constexpr int RR = NM / (NQ + 1) > 0 ? NM / (NQ + 1) : 1;
+      // DMA instruction q goes out after MFMA pos(q) = min((q + 1) RR, NM) - 1.
 #pragma unroll
-      for (int ks = 0; ks < KS - 1; ++ks) {
-        load_frags(b, ks + 1, (ks + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_step(ks & 1);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int m = 0; m < NM; ++m) {
+        Tr::mma(acc[m / FN][m % FN], bf[s][m % FN], af[s][m / FN]);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int pos = (q + 1) * RR < NM ? (q + 1) * RR - 1 : NM - 1;
+          if (pos == m) dma_one(kt, buf, q0 + q);
+        }
       }
+      if constexpr (true && NQ > 0) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            const int pos = (q + 1) * RR < NM ? (q + 1) * RR - 1 : NM - 1;
+            if (pos == m) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+        }
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using IP0 = std::integral_constant<int, NP0>;
+    using IP1 = std::integral_constant<int, NP1>;
+    using IP2 = std::integral_constant<int, NP2>;
+    // k-tile kl from buffer kl % 2. DMA of k-tile kl+1 (buffer b ^ 1): part 0 went out in the
+    // previous k-tile's last k-step, parts 1 and 2 go out during k-steps 0 and 1 here; the
+    // barrier before k-step 3 waits for it, and part 0 of k-tile kl+2 follows the barrier.
+    auto body = [&](int kl, auto has1, auto has2) {
+      const int b = kl & 1;
+      // This k-tile's first fragments were read a whole k-step ago: waiting for them here is
+      // free and leaves only the next k-step's reads pending below.
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      load_frags(b, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(has1)::value) kstep(0, k_begin + kl + 1, b ^ 1, NP0, IP1{});
+      else kstep(0, 0, 0, 0, I0{});
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(b, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(has1)::value) kstep(1, k_begin + kl + 1, b ^ 1, NP0 + NP1, IP2{});
+      else kstep(1, 0, 0, 0, I0{});
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(b, 3, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      kstep(0, 0, 0, 0, I0{});
+      __builtin_amdgcn_sched_barrier(0);
       // k-tile kl+1 has landed and every wave's reads of buffer b are done.
       block_sync();
-      if (kl + 2 < KL) issue(k_begin + kl + 2, b);
       load_frags(b ^ 1, 0, 0);   // after the last k-tile: a harmless read of the idle buffer
       __builtin_amdgcn_sched_barrier(0);
-      mma_step((KS - 1) & 1);
+      if constexpr (decltype(has2)::value) kstep(1, k_begin + kl + 2, b, 0, IP0{});
+      else kstep(1, 0, 0, 0, I0{});
       __builtin_amdgcn_sched_barrier(0);
+    };
+    using T1 = std::true_type;
+    using F1 = std::false_type;
+    issue(k_begin, 0);
+    if (KL > 1) {
+#pragma unroll
+      for (int q = 0; q < NP0; ++q) dma_one(k_begin + 1, 1, q);
     }
+    block_sync();
+    load_frags(0, 0, 0);
+    int kl = 0;
+    for (; kl + 2 < KL; ++kl) body(kl, T1{}, T1{});
+    if (kl + 1 < KL) body(kl++, T1{}, F1{});
+    body(kl, F1{}, F1{});
     if (slot >= 0) {
       floatx4* P = reinterpret_cast<floatx4*>(p.partial) + (int64_t)slot * TILE_F4;
 #pragma unroll
