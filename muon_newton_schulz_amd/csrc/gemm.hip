@@ -704,12 +704,12 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
                      s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split < 2) return e;
-  // The tail epilogue reads all parts of a tile itself when they are few (<= 1 MiB per
-  // tile); more are first summed by a wide reduction launch.
+  // The tail epilogue (one block per 64 x 64 sub-tile) sums the parts itself when they are
+  // few (at most 8, 128 KiB per block); more are first summed by a wide reduction launch.
   constexpr int tile_f4 = BM * BN / 4;
   static_assert(tile_f4 % 256 == 0, "whole reduce blocks per tile");
   a.fix_parts = split;
-  if ((int64_t)split * tile_f4 * 16 > (int64_t(1) << 20)) {
+  if (split > 8) {
     hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)(tail * (tile_f4 / 256))), dim3(256), 0, s,
                        reinterpret_cast<floatx4*>(a.partial), split, tile_f4);
     e = hipGetLastError();
