@@ -410,6 +410,7 @@ __global__ __launch_bounds__(kFinThreads) void k_normuon_finalize(
   for (int64_t i = threadIdx.x; i < rows; i += kFinThreads) {
     float r4[4] = {0.f, 0.f, 0.f, 0.f};
     int c = 0;
+#pragma unroll 4
     for (; c + 4 <= chunks; c += 4) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) r4[q] += pt[(int64_t)(c + q) * rows + i];
@@ -560,18 +561,31 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 // Exclusive prefix sum over the block (kSelThreads values), deterministic.
 __device__ int block_exclusive_scan(int v, int* sh) {
-  const int t = threadIdx.x;
-  sh[t] = v;
-  __syncthreads();
-  for (int o = 1; o < kSelThreads; o <<= 1) {
-    const int add = t >= o ? sh[t - o] : 0;
-    __syncthreads();
-    sh[t] += add;
-    __syncthreads();
+  // integer sums are exact, so the result does not depend on the order of the additions:
+  // a shuffle scan inside each wave, then one over the wave totals
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  const int incl = sh[t];
+  if (lane == 63) sh[w] = x;
   __syncthreads();
-  return incl - v;
+  if (w == 0) {
+    const int tot = lane < kSelWaves ? sh[lane] : 0;
+    int y = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int z = __shfl_up(y, o, 64);
+      if (lane >= o) y += z;
+    }
+    if (lane < kSelWaves) sh[64 + lane] = y - tot;
+  }
+  __syncthreads();
+  const int res = x - v + sh[64 + w];
+  __syncthreads();
+  return res;
 }
 
 __global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, int64_t rows, int64_t k,
@@ -598,15 +612,16 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, int64_t r
       hist[0][t] = c;
     }
     __syncthreads();
-    if (t == 0) {
-      int64_t above = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (above + (int64_t)hist[0][d] >= remaining) break;
-        above += hist[0][d];
+    // The digit of the k-th largest key: with digits in descending order (thread t holds
+    // digit 255 - t), `above` counts the keys with a larger digit; exactly one digit has
+    // above < remaining <= above + count.
+    {
+      const int cnt = t < 256 ? (int)hist[0][255 - t] : 0;
+      const int above = block_exclusive_scan(cnt, scan_sh);
+      if (t < 256 && (int64_t)above < remaining && (int64_t)above + cnt >= remaining) {
+        sh_prefix = prefix | ((uint32_t)(255 - t) << shift);
+        sh_remaining = remaining - above;
       }
-      sh_prefix = prefix | ((uint32_t)d << shift);
-      sh_remaining = remaining - above;
     }
     __syncthreads();
     prefix = sh_prefix;

@@ -192,6 +192,26 @@ def test_dion3_selection_matches_oracle():
     assert sorted(moved.tolist()) == sorted(S.tolist())
 
 
+def test_dion3_selection_all_ties():
+    """Every row has the same l1 norm (identical rows): each radix pass ties on every key,
+    and the k rows of lowest index are taken (k = ceil(300 / 4) = 75)."""
+    _say("case dion3 all ties")
+    rows, cols = 300, 64
+    rng = np.random.default_rng(8)
+    G = np.tile(rng.standard_normal((1, cols)).astype(np.float32), (rows, 1))
+    W = torch.zeros(rows, cols, device="cuda")
+    M = torch.zeros(rows, cols, device="cuda")
+    mns.muon_step(W, M, torch.from_numpy(G).cuda(), mu=0.5, lr=0.1, coeffs=[QUINTIC] * 5,
+                  kind="gram", restart_before=(3,), row_fraction=0.25)
+    torch.cuda.synchronize()
+    want = oracle.select_rows(G.astype(np.float64), 75)
+    assert sorted(want.tolist()) == list(range(75))
+    moved = np.where(W.cpu().numpy().any(axis=1))[0]
+    assert moved.tolist() == list(range(75))
+    decayed = np.where(np.isclose(M.cpu().numpy(), 0.5 * G).all(axis=1))[0]
+    assert decayed.tolist() == list(range(75))
+
+
 @pytest.mark.parametrize("storage", ["bf16", "f32"])
 def test_normuon_scale(storage):
     _say("case normuon", storage)
