@@ -61,14 +61,19 @@ def build_inputs(wl, torch, np, synthetic, dev):
     return W, M, G, V
 
 
-GEMM_SOURCE = os.path.join(ROOT, "muon_newton_schulz_amd", "csrc", "gemm.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "muon_newton_schulz_amd", "csrc", f)
+                for f in ("gemm.hip", "gemm_epilogue.inc")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def source_digest(path: str) -> str:
+def source_digest(paths) -> str:
+    """sha256[:16] over the concatenated GEMM sources (the kernel the counters were taken on)."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -80,7 +85,7 @@ def measured_traffic(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     ent = t.get("kernels", {}).get(f"{workload}::{kernel}")
-    if not ent or t.get("gemm_source_sha256_16") != source_digest(GEMM_SOURCE):
+    if not ent or t.get("gemm_source_sha256_16") != source_digest(GEMM_SOURCES):
         return None
     return ent.get("bytes_per_launch")
 

@@ -106,6 +106,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, u32x4* dst, int 
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
 constexpr int kWaitVm0Lgkm0 = 0x0070;     // vmcnt(0) lgkmcnt(0)
+// vmcnt(n) alone (n < 64): at most n of this wave's vector-memory operations outstanding
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 __device__ __forceinline__ void block_sync() {
   // All of this wave's LDS-DMA writes and LDS accesses are done, then the workgroup meets.
@@ -146,6 +148,7 @@ __device__ __forceinline__ void load4<float>(const float* p, float* v) {
   const float4 f = *reinterpret_cast<const float4*>(p);
   v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
 }
+
 
 // The product: whole tiles with their epilogue, and the k-parts of split tiles (float32
 // partial sums, finished by k_tail_epilogue).
@@ -391,112 +394,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   }
 
   // ---- epilogue: v = alpha acc + beta D + gamma I, staged through LDS ----
-  // acc[i][j][4g + e] is element (m, n + e) with m = wm*WM + 32i + (lane & 31) and
-  // n = wn*WN + 32j + 8g + 4(lane >> 5) (tile-local).
-  const T* Dg = p.D ? static_cast<const T*>(p.D) + bz * p.sD : nullptr;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int ml = wm * WM + 32 * i + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wn * WN + 32 * j + 8 * g + 4 * (lane >> 5);
-        float d[4] = {0.f, 0.f, 0.f, 0.f};
-        if (Dg) load4<T>(Dg + (int64_t)(m0 + ml) * p.ldd + n0 + nl, d);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = p.alpha * acc[i][j][4 * g + e] + p.beta * d[e];
-          if (m0 + ml == n0 + nl + e && m0 + ml < p.diag_limit) v += p.gamma;
-          acc[i][j][4 * g + e] = v;
-        }
-      }
-    }
-  }
-
-  T* tile = reinterpret_cast<T*>(&lds[0]);
-  constexpr int CPR_N = BN * ES / 16;     // 16-byte chunks per tile row of [m][n]
-  constexpr int CPR_M = BM * ES / 16;     // ... of [n][m]
-  constexpr int EPC = 16 / ES;            // elements per chunk
-  const bool diag_tile = SYM && (tm == tn);
-
-  // Row pass: tile as [m][n] (chunk c of row m at c ^ (m % CPR_N)), then 16-byte rows to C.
-  if (SYM || p.C) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int ml = wm * WM + 32 * i + (lane & 31);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int nl = wn * WN + 32 * j + 8 * g + 4 * (lane >> 5);
-          const int c = nl / EPC, within = nl % EPC;
-          T* dst = tile + ml * BN + (c ^ (ml % CPR_N)) * EPC + within;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = (T)acc[i][j][4 * g + e];
-        }
-      }
-    }
-    block_sync();
-    T* Cg = static_cast<T*>(p.C) + bz * p.sC;
-    for (int q = tid; q < BM * CPR_N; q += NT) {
-      const int ml = q / CPR_N, c = q % CPR_N;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(tile + ml * BN + (c ^ (ml % CPR_N)) * EPC);
-      T* dst = Cg + (int64_t)(m0 + ml) * p.ldc + n0 + c * EPC;
-      // a diagonal tile keeps its upper triangle here: whole chunks right of the diagonal,
-      // element by element in the chunk that holds it, nothing left of it
-      if (!diag_tile || c * EPC >= ml) {
-        *reinterpret_cast<u32x4*>(dst) = v;
-      } else if (c * EPC + EPC > ml) {
-        const T* vs = reinterpret_cast<const T*>(&v);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e)
-          if (ml <= c * EPC + e) dst[e] = vs[e];
-      }
-    }
-    block_sync();
-  }
-
-  // Transposed pass: tile as [n][m], then 16-byte rows to C^T (dense) or to the mirrored
-  // tile C[n0.., m0..] (sym; in a diagonal tile only its strictly lower part).
-  if (SYM || p.Ct) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int ml = wm * WM + 32 * i + (lane & 31);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int nl = wn * WN + 32 * j + 8 * g + 4 * (lane >> 5);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) tile[(nl + e) * BM + ml] = (T)acc[i][j][4 * g + e];
-        }
-      }
-    }
-    block_sync();
-    T* Tg;
-    int64_t ldt;
-    if (SYM) {
-      Tg = static_cast<T*>(p.C) + bz * p.sC;
-      ldt = p.ldc;
-    } else {
-      Tg = static_cast<T*>(p.Ct) + bz * p.sCt;
-      ldt = p.ldct;
-    }
-    for (int q = tid; q < BN * CPR_M; q += NT) {
-      const int nl = q / CPR_M, c = q % CPR_M;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(tile + nl * BM + c * EPC);
-      T* dst = Tg + (int64_t)(n0 + nl) * ldt + m0 + c * EPC;
-      // a diagonal tile's mirror fills only the strictly lower triangle
-      if (!diag_tile || c * EPC + EPC <= nl) {
-        *reinterpret_cast<u32x4*>(dst) = v;
-      } else if (c * EPC < nl) {
-        const T* vs = reinterpret_cast<const T*>(&v);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e)
-          if (c * EPC + e < nl) dst[e] = vs[e];
-      }
-    }
+  {
+    T* tile = reinterpret_cast<T*>(&lds[0]);
+#include "gemm_epilogue.inc"
   }
 }
 
@@ -662,7 +562,194 @@ int cu_count() {
   return n;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, bool SYM>
+// Small grids (64 x 64 tiles, few tiles per CU): the four waves of a block split the block's
+// k-range among themselves (wave w takes k-tiles w, w + 4, ...), each computing the whole
+// 64 x 64 tile from its own double-buffered LDS stages with no barriers in the k loop; the four
+// partial tiles are then added in wave order through LDS, each wave keeping the quarter the
+// 2 x 2 wave layout gives it, and the usual epilogue (or partial-sum store) follows. A k loop
+// of KL k-tiles takes about KL / 4 steps of load latency instead of KL.
+template <typename T, bool SYM>
+__global__ __launch_bounds__(256) void k_gemm_kw(GemmArgs p) {
+  using Tr = Traits<T>;
+  constexpr int BM = 64, BN = 64, NT = 256;
+  constexpr int VEC = Tr::VEC, BK = Tr::BK, ES = (int)sizeof(T);
+  constexpr int ROWS = BM + BN;                 // LDS rows of one stage (A rows, then B rows)
+  constexpr int WSTAGE = ROWS * kChunks;        // u32x4 per stage
+  constexpr int INST = ROWS / 8;                // DMA instructions per wave per k-tile
+  __shared__ u32x4 lds[4 * 2 * WSTAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int KT = p.K / BK;
+  int lin = blockIdx.x, k_begin = 0, k_end = KT, slot = -1;
+  if (lin < p.full_blocks) {
+    const int q = p.full_blocks / 8;
+    if (lin < 8 * q) lin = (lin % 8) * q + lin / 8;
+  } else {
+    const int r = lin - p.full_blocks, part = r % p.split;
+    lin = p.full_blocks + r / p.split;
+    slot = r;
+    k_begin = (int)((int64_t)part * KT / p.split);
+    k_end = (int)((int64_t)(part + 1) * KT / p.split);
+  }
+  lin = __builtin_amdgcn_readfirstlane(lin);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  k_begin = __builtin_amdgcn_readfirstlane(k_begin);
+  k_end = __builtin_amdgcn_readfirstlane(k_end);
+  int tm, tn;
+  int64_t bz;
+  tile_coords<SYM, BM>(p, lin, tm, tn, bz);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const char* Abase = static_cast<const char*>(p.A) + (bz * p.sA + (int64_t)m0 * p.lda) * ES;
+  const char* Bbase = static_cast<const char*>(p.B) + (bz * p.sB + (int64_t)n0 * p.ldb) * ES;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase, ((int64_t)(p.M - m0) * p.lda) * ES);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase, ((int64_t)(p.N - n0) * p.ldb) * ES);
+  // instruction i fills LDS rows 8i .. 8i+7 of the wave's stage (rows < BM: A, else B)
+  int off[INST];
+#pragma unroll
+  for (int i = 0; i < INST; ++i) {
+    const int row = i * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ ((row ^ ((row >> 3) & 3)) & 7);
+    off[i] = row < BM ? (row * (int)p.lda + ch * VEC) * ES
+                      : ((row - BM) * (int)p.ldb + ch * VEC) * ES;
+  }
+  u32x4* const wlds = lds + wave * 2 * WSTAGE;
+  auto issue = [&](int kt, int st) {
+    const int so = kt * BK * ES;
+#pragma unroll
+    for (int i = 0; i < INST; ++i)
+      dma16(i * 8 < BM ? rA : rB, &wlds[st * WSTAGE + i * 8 * kChunks], off[i], so);
+  };
+
+  floatx16 acc4[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc4[i][j][e] = 0.f;
+  u32x4 af[2][2], bf[2][2];
+  auto load_frags = [&](int st, int ks, int sl) {
+    const int ch = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) af[sl][i] = wlds[st * WSTAGE + swz(32 * i + (lane & 31), ch)];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bf[sl][j] = wlds[st * WSTAGE + swz(BM + 32 * j + (lane & 31), ch)];
+  };
+  auto mma_step = [&](int sl) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) Tr::mma(acc4[i][j], bf[sl][j], af[sl][i]);
+  };
+
+  // This wave's k-tiles: k_begin + wave + 4 j, j < nk. Two are in flight: the load of the
+  // wave's k-tile j+2 goes into stage j % 2 once the last k-step of k-tile j is in registers.
+  const int KL = k_end - k_begin;
+  const int nk = KL > wave ? (KL - wave + 3) / 4 : 0;
+  constexpr int KS = kChunks / 2;
+  if (nk > 0) {
+    issue(k_begin + wave, 0);
+    if (nk > 1) {
+      issue(k_begin + wave + 4, 1);
+      __builtin_amdgcn_s_waitcnt(wait_vm(INST));   // k-tile 0 has landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+    }
+    asm volatile("" ::: "memory");
+    load_frags(0, 0, 0);
+    for (int j = 0; j < nk; ++j) {
+      const int st = j & 1;
+#pragma unroll
+      for (int ks = 0; ks < KS - 1; ++ks) {
+        load_frags(st, ks + 1, (ks + 1) & 1);
+        mma_step(ks & 1);
+      }
+      // k-step 3's fragments in registers, so stage st is free; k-tile j+1 must have landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      if (j + 2 < nk) {
+        issue(k_begin + wave + 4 * (j + 2), st);
+        __builtin_amdgcn_s_waitcnt(wait_vm(INST));   // k-tile j+1 has landed
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+      }
+      asm volatile("" ::: "memory");
+      if (j + 1 < nk) load_frags(st ^ 1, 0, 0);
+      mma_step((KS - 1) & 1);
+    }
+  }
+
+  // Sum the four partial tiles in wave order; wave w keeps fragment (w / 2, w % 2).
+  block_sync();
+  floatx4* ex = reinterpret_cast<floatx4*>(lds);   // [owner][source][g][lane]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int owner = 2 * i + j;
+      if (owner == wave) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        floatx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc4[i][j][4 * g + e];
+        ex[((owner * 4 + wave) * 4 + g) * 64 + lane] = v;
+      }
+    }
+  block_sync();
+  floatx16 acc[1][1];
+  {
+    const int wi = wave >> 1, wj = wave & 1;
+    floatx16 own;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (i == wi && j == wj) own = acc4[i][j];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      floatx4 sum;
+#pragma unroll
+      for (int src = 0; src < 4; ++src) {
+        floatx4 v;
+        if (src == wave) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = own[4 * g + e];
+        } else {
+          v = ex[((wave * 4 + src) * 4 + g) * 64 + lane];
+        }
+        sum = src == 0 ? v : sum + v;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[0][0][4 * g + e] = sum[e];
+    }
+  }
+
+  if (slot >= 0) {
+    // partial sums in the fragment order of the 2 x 2 layout (what k_tail_epilogue reads)
+    floatx4* P = reinterpret_cast<floatx4*>(p.partial) + (int64_t)slot * (4 * NT);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      floatx4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[0][0][4 * g + e];
+      P[g * NT + tid] = v;
+    }
+    return;
+  }
+  block_sync();
+  {
+    constexpr int WM = 32, WN = 32, FM = 1, FN = 1;   // the 2 x 2 wave layout
+    const int wm = wave >> 1, wn = wave & 1;
+    T* tile = reinterpret_cast<T*>(&lds[0]);
+#include "gemm_epilogue.inc"
+  }
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, bool SYM, bool KW = false>
 hipError_t launch(const GemmDesc& d, hipStream_t s) {
   GemmArgs a;
   a.A = d.A; a.B = d.B; a.D = d.D; a.C = d.C; a.Ct = d.Ct;
@@ -681,10 +768,10 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
     a.tiles_per_batch = (d.M / BM) * (d.N / BN);
   }
   // Rounds of whole tiles over the CU slots (one 256-tile block per CU, two 128-tile blocks,
-  // four 64-tile blocks);
-  // a tail round less than half full is split along k (at least 8 k-tiles per part).
+  // one 64-tile block of k_gemm_kw); a tail round less than half full is split along k (at
+  // least 8 k-tiles per part).
   const int64_t total = (int64_t)a.tiles_per_batch * d.batch;
-  const int slots = cu_count() * (BM >= 256 ? 1 : BM >= 128 ? 2 : 4);
+  const int slots = cu_count() * (KW || BM >= 256 ? 1 : BM >= 128 ? 2 : 4);
   const int64_t rounds = total / slots, tail = total % slots;
   const int KT = d.K / Traits<T>::BK;
   int split = 1;
@@ -700,8 +787,11 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   a.fix_parts = split;
   a.full_blocks = (int)(split > 1 ? rounds * slots : total);
   const unsigned blocks = (unsigned)(a.full_blocks + (split > 1 ? tail * split : 0));
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM>), dim3(blocks), dim3(64 * WGM * WGN), 0,
-                     s, a);
+  if constexpr (KW)
+    hipLaunchKernelGGL((k_gemm_kw<T, SYM>), dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM>), dim3(blocks), dim3(64 * WGM * WGN), 0,
+                       s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split < 2) return e;
   // The tail epilogue (one block per 64 x 64 sub-tile) sums the parts itself when they are
@@ -751,7 +841,10 @@ hipError_t gemm(const GemmDesc& d, hipStream_t s) {
   if (d.elem == Elem::F32) return dispatch_tile<float, 128, 2, 2>(d, s);
   const int bt = tile_for(d);
   if (bt == 256) return dispatch_tile<_Float16, 256, 2, 4>(d, s);
-  if (bt == 64) return dispatch_tile<_Float16, 64, 2, 2>(d, s);
+  if (bt == 64) {
+    if (d.sym) return launch<_Float16, 64, 64, 2, 2, true, true>(d, s);
+    return launch<_Float16, 64, 64, 2, 2, false, true>(d, s);
+  }
   return dispatch_tile<_Float16, 128, 2, 2>(d, s);
 }
 
