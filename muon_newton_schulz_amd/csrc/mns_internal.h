@@ -19,7 +19,7 @@ inline int elem_bytes(Elem e) { return e == Elem::F16 ? 2 : 4; }
 
 // Caller pointers of up to kMaxPack same-shape matrices, passed by value as a kernel
 // argument (no device-side pointer table, nothing to upload).
-constexpr int kMaxPack = 16;
+constexpr int kMaxPack = 32;
 struct PtrPack {
   void* p[kMaxPack];
 };

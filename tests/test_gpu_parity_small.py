@@ -160,9 +160,9 @@ def test_muon_step_gram_kind(storage):
 
 
 def test_muon_step_many_matrices_one_shape():
-    """More matrices of one shape than one batched launch holds (chunking)."""
-    _say("case 20 x 128x384")
-    _step_case([(128, 384)] * 20, "bf16", "standard", (), True, 1.0, 20, w_zero=True)
+    """More matrices of one shape than one batched launch holds (32: chunking)."""
+    _say("case 40 x 128x384")
+    _step_case([(128, 384)] * 40, "bf16", "standard", (), True, 1.0, 20, w_zero=True)
 
 
 @pytest.mark.parametrize("shape,f", [((64, 200), 0.25), ((200, 64), 0.5), ((100, 300), 1.0 / 3)])
