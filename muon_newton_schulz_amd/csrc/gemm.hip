@@ -823,10 +823,11 @@ int64_t tiles_of(const GemmDesc& d, int bt) {
   return d.sym ? tm * (tm + 1) / 2 : tm * tn;
 }
 
-// 256 x 256 tiles when they give at least two rounds of blocks over the CUs; 64 x 64 when
-// 128 x 128 tiles would not even fill a quarter of the CUs; else 128 x 128.
+// 256 x 256 tiles when they give at least two rounds of blocks over the CUs; 64 x 64 (the
+// k-split kernel) when 128 x 128 tiles would not even fill a quarter of the CUs; else
+// 128 x 128. Float32 uses the same rule without the 256 x 256 step.
 int tile_for(const GemmDesc& d) {
-  if (d.elem == Elem::F32) return 128;
+  if (d.elem == Elem::F32) return tiles_of(d, 128) * d.batch * 4 < cu_count() ? 64 : 128;
   if (tiles_of(d, 256) * d.batch >= 2 * cu_count()) return 256;
   if (tiles_of(d, 128) * d.batch * 4 < cu_count()) return 64;
   return 128;
@@ -838,7 +839,13 @@ hipError_t gemm(const GemmDesc& d, hipStream_t s) {
   if (d.M % kPad || d.N % kPad || d.K % kPad || d.batch < 1) return hipErrorInvalidValue;
   if (d.sym && (d.M != d.N || !d.C || d.Ct)) return hipErrorInvalidValue;
   if (!d.sym && !d.C && !d.Ct) return hipErrorInvalidValue;
-  if (d.elem == Elem::F32) return dispatch_tile<float, 128, 2, 2>(d, s);
+  if (d.elem == Elem::F32) {
+    if (tile_for(d) == 64) {
+      if (d.sym) return launch<float, 64, 64, 2, 2, true, true>(d, s);
+      return launch<float, 64, 64, 2, 2, false, true>(d, s);
+    }
+    return dispatch_tile<float, 128, 2, 2>(d, s);
+  }
   const int bt = tile_for(d);
   if (bt == 256) return dispatch_tile<_Float16, 256, 2, 4>(d, s);
   if (bt == 64) {
@@ -849,7 +856,10 @@ hipError_t gemm(const GemmDesc& d, hipStream_t s) {
 }
 
 const char* gemm_name(const GemmDesc& d) {
-  if (d.elem == Elem::F32) return d.sym ? "gemm_sym_f32_128" : "gemm_nt_f32_128";
+  if (d.elem == Elem::F32) {
+    if (tile_for(d) == 64) return d.sym ? "gemm_sym_f32_64" : "gemm_nt_f32_64";
+    return d.sym ? "gemm_sym_f32_128" : "gemm_nt_f32_128";
+  }
   switch (tile_for(d)) {
     case 256: return d.sym ? "gemm_sym_f16_256" : "gemm_nt_f16_256";
     case 64: return d.sym ? "gemm_sym_f16_64" : "gemm_nt_f16_64";
