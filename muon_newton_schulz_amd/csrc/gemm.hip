@@ -45,6 +45,10 @@
 //     adds each tile's partials in a fixed order (a wide reduction launch first when they
 //     are many) and runs the same epilogue on the sums (deterministic, no inter-block
 //     waiting).
+//   * Small grids (64 x 64 tiles) run k_gemm_kw instead: the four waves of a block split the
+//     block's k-range, each with its own LDS stages and no barrier in the k loop, and add
+//     their partial tiles in wave order before the same epilogue (gemm_epilogue.inc, which
+//     both kernels expand inline).
 #include "mns_internal.h"
 
 #include <type_traits>
