@@ -67,12 +67,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_digest(paths) -> str:
-    """sha256[:16] over the concatenated GEMM sources (the kernel the counters were taken on)."""
+    """sha256[:16] over the concatenated GEMM sources with // comments and whitespace
+    removed: it changes when the kernel code does, not when its comments do."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for path in paths:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            for line in f:
+                code = re.sub(r"\s+", "", re.sub(r"//.*", "", line))
+                if code:
+                    h.update(code.encode())
     return h.hexdigest()[:16]
 
 
