@@ -38,7 +38,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
     ap.add_argument("--graph", action="store_true",
-                    help="also time the step captured once in a HIP graph and replayed")
+                    help="(default) also time the step captured once in a HIP graph and replayed")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP graph replay timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -263,7 +265,7 @@ def main():
                 "traffic": measured_traffic(dom["name"], f"config{args.config}-{kind}")}
 
     graph = None
-    if args.graph:
+    if not args.no_graph:
         graph = graph_timing(mns, torch, step_args=(W, M, G, v_arg), ws=ws, kw=kw,
                              warmup=args.warmup, steps=args.steps)
         graph["eager_ms_per_step"] = round(ms_step, 4)
