@@ -178,11 +178,27 @@ GemmDesc left_desc(const Geo& g, int count, const NsBuffers& b, const void* L, c
   return d;
 }
 
+// Optional request for the per-row sums of squares of the NS result (NorMuon's row
+// statistics), taken in the epilogue of the product that writes the result: part gets the
+// GemmDesc::rowsq layout (64-column chunks); done reports whether such a product ran.
+struct RowSq {
+  float* part = nullptr;
+  int rows = 0;
+  bool done = false;
+};
+
+void want_rowsq(GemmDesc& d, RowSq* rs) {
+  if (!rs) return;
+  d.rowsq = rs->part;
+  d.rowsq_rows = rs->rows;
+  rs->done = true;
+}
+
 // Standard quintic NS on the normalised iterate (b.X[0], b.Xt[0]) (section "Standard
 // Newton-Schulz"): A = X X^T, B = b A + c A^2, X <- a X + B X. Returns the result in the
 // stored layout (X for a wide matrix, X^T for a tall one; row pitch padded_ld(cols_p)).
 mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, const float* abc,
-                        hipStream_t s, void** out) {
+                        hipStream_t s, void** out, RowSq* rs) {
   int cur = 0;
   void* A = b.sq[0];
   void* B = b.sq[1];
@@ -212,6 +228,7 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
       upd.beta = a;
       upd.D = b.X[cur]; upd.ldd = g.ld_x; upd.sD = b.x_stride;   // read in C coordinates
     }
+    if (last) want_rowsq(upd, rs);
     MNS_HIP(timed_gemm(upd, 2.0 * nn * g.m, s));
     cur ^= 1;
   }
@@ -223,7 +240,7 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
 // Z = a I + b R + c R^2, R <- R Z^2 (skipped when unused), Q <- Q Z (Q_1 = Z_1);
 // a restart before t forms X <- Q X, R <- X X^T, Q <- I. Output Q X (stored layout).
 mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const float* abc,
-                    uint32_t restart_mask, hipStream_t s, void** out) {
+                    uint32_t restart_mask, hipStream_t s, void** out, RowSq* rs) {
   int cur = 0;
   void* R = b.sq[0];
   void* Rt = b.sq[1];
@@ -275,18 +292,19 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
   if (q_identity) {
     *out = g.tall ? b.Xt[cur] : b.X[cur];
   } else {
-    MNS_HIP(timed_gemm(left_desc(g, count, b, Q, b.Xt[cur], g.tall ? nullptr : b.X[cur ^ 1],
-                                 g.tall ? b.Xt[cur ^ 1] : nullptr),
-                       2.0 * nn * g.m, s));
+    GemmDesc fin = left_desc(g, count, b, Q, b.Xt[cur], g.tall ? nullptr : b.X[cur ^ 1],
+                             g.tall ? b.Xt[cur ^ 1] : nullptr);
+    want_rowsq(fin, rs);
+    MNS_HIP(timed_gemm(fin, 2.0 * nn * g.m, s));
     *out = g.tall ? b.Xt[cur ^ 1] : b.X[cur ^ 1];
   }
   return MNS_OK;
 }
 
 mns_status run_ns(const Geo& g, int count, const NsBuffers& b, int kind, int T, const float* abc,
-                  uint32_t restart_mask, hipStream_t s, void** out) {
-  if (kind == MNS_NS_GRAM) return run_gram(g, count, b, T, abc, restart_mask, s, out);
-  return run_standard(g, count, b, T, abc, s, out);
+                  uint32_t restart_mask, hipStream_t s, void** out, RowSq* rs = nullptr) {
+  if (kind == MNS_NS_GRAM) return run_gram(g, count, b, T, abc, restart_mask, s, out, rs);
+  return run_standard(g, count, b, T, abc, s, out, rs);
 }
 
 // ---- validation helpers --------------------------------------------------------------------
@@ -411,7 +429,7 @@ size_t carve_step(void* base, const Geo& g, int count, int64_t rows, int64_t col
   w.partials = cv.take<float>((size_t)count * w.nblk);
   w.xscale = cv.take<float>((size_t)count);
   carve_ns(cv, g, count, kind, w.ns);
-  w.chunks = (int)(g.cols_p / kPad);                   // row-norm partials per stored row
+  w.chunks = (int)(g.cols_p / 64);                     // row-norm partials per stored row
   w.part = cv.take<float>((size_t)count * w.chunks * g.rows);
   w.rowscale = cv.take<float>((size_t)count * g.rows);
   if (dion) {
@@ -517,12 +535,17 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
                            straight(g, w.ns), transposed(g, w.ns), g.rows_p, g.cols_p, s); }));
       }
       void* O = nullptr;
-      st = run_ns(g, c, w.ns, hp->kind, hp->T, hp->abc, hp->restart_mask, s, &O);
+      RowSq rs;
+      rs.part = w.part;
+      rs.rows = (int)k;
+      st = run_ns(g, c, w.ns, hp->kind, hp->T, hp->abc, hp->restart_mask, s, &O,
+                  hp->normuon ? &rs : nullptr);
       if (st != MNS_OK) return st;
       const float inv_s = 1.0f / g.S;
       if (hp->normuon) {
-        MNS_HIP(timed("row_sumsq", 0, sel * es, s, [&] {
-          return row_sumsq_x(O, g.elem, g.rows_p, g.cols_p, c, k, cols, w.part, s); }));
+        // The row statistics come from the epilogue of the product that wrote the result
+        // (every run ends with one: T >= 1).
+        if (!rs.done) return MNS_ERR_PARAM;
         MNS_HIP(timed("normuon_finalize", 0, 4.0 * c * k * (w.chunks + 3), s, [&] {
           return normuon_finalize(w.part, w.chunks, c, k, cols, &Vp, nullptr, 0,
                                   dion ? w.S : nullptr, hp->beta2, hp->eps, inv_s * inv_s, inv_s,

@@ -338,40 +338,6 @@ __global__ __launch_bounds__(kThreads) void k_export(const TX* X, int64_t rows_p
 
 // ---- NorMuon statistics: per stored row, partial sums of O^2 -------------------------------
 
-// One block per 64 x 256 tile of the iterate in the stored layout: partial sums of each
-// row's squares over the tile's 256 columns -> part[chunk = tile column][row]. 32 threads
-// (8 elements each) per row; 8 rows per pass, 8 passes with all loads in flight.
-constexpr int kRsRows = 64;
-
-template <typename TX>
-__global__ __launch_bounds__(kThreads) void k_row_sumsq_x(const TX* X, int64_t rows_p,
-                                                          int64_t cols_p, int64_t rows,
-                                                          float* part) {
-  constexpr int TPR = 32;                 // threads per 256-wide row chunk
-  constexpr int RPI = kThreads / TPR;     // rows per pass
-  const int b = blockIdx.z;
-  const int64_t ldx = padded_ld(cols_p);
-  const TX* x = X + (int64_t)b * rows_p * ldx;
-  const int64_t r0 = (int64_t)blockIdx.y * kRsRows;
-  const int64_t c = (int64_t)blockIdx.x * 256 + (threadIdx.x % TPR) * 8;
-  const int64_t chunks = cols_p / 256;
-  float* out = part + (int64_t)b * chunks * rows + (int64_t)blockIdx.x * rows;
-  f8 v[kRsRows / RPI];
-#pragma unroll
-  for (int it = 0; it < kRsRows / RPI; ++it)
-    v[it] = load8<TX>(x, (r0 + it * RPI + threadIdx.x / TPR) * ldx + c);
-#pragma unroll
-  for (int it = 0; it < kRsRows / RPI; ++it) {
-    const int64_t r = r0 + it * RPI + threadIdx.x / TPR;
-    float s = v[it].lo.x * v[it].lo.x + v[it].lo.y * v[it].lo.y + v[it].lo.z * v[it].lo.z +
-              v[it].lo.w * v[it].lo.w + v[it].hi.x * v[it].hi.x + v[it].hi.y * v[it].hi.y +
-              v[it].hi.z * v[it].hi.z + v[it].hi.w * v[it].hi.w;
-#pragma unroll
-    for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_down(s, o, TPR);
-    if ((threadIdx.x % TPR) == 0 && r < rows) out[r] = s;
-  }
-}
-
 // Caller-layout O (rows x cols): one block per row, part[b][0][row].
 template <typename TO>
 __global__ __launch_bounds__(kThreads) void k_row_sumsq_stored(const TO* O, int64_t rows,
@@ -783,19 +749,6 @@ hipError_t export_output(const void* X, Elem e, int64_t rows_p, int64_t cols_p, 
     if (st == Store::BF16) launch_export<float, uint16_t>(X, rows_p, cols_p, count, rows, cols, inv_s, O, s);
     else launch_export<float, float>(X, rows_p, cols_p, count, rows, cols, inv_s, O, s);
   }
-  return last();
-}
-
-hipError_t row_sumsq_x(const void* X, Elem e, int64_t rows_p, int64_t cols_p, int count,
-                       int64_t rows, int64_t cols, float* part, hipStream_t s) {
-  (void)cols;
-  dim3 grid((unsigned)(cols_p / 256), (unsigned)(rows_p / kRsRows), count);
-  if (e == Elem::F16)
-    hipLaunchKernelGGL(k_row_sumsq_x<_Float16>, grid, dim3(kThreads), 0, s,
-                       static_cast<const _Float16*>(X), rows_p, cols_p, rows, part);
-  else
-    hipLaunchKernelGGL(k_row_sumsq_x<float>, grid, dim3(kThreads), 0, s,
-                       static_cast<const float*>(X), rows_p, cols_p, rows, part);
   return last();
 }
 

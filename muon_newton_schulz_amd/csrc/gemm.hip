@@ -137,7 +137,28 @@ struct GemmArgs {
   int split;        // k-parts per split tile
   float* partial;   // split partial sums, BM*BN floats per (tile, part)
   int fix_parts;    // parts the epilogue launch adds (split, or 1 after k_reduce_parts)
+  float* rowsq;     // per-row sums of squares of the stored output (or null)
+  int rowsq_rows, rowsq_chunks;
 };
+
+// Sum of the squares of one 16-byte chunk of stored output values, added over the RS_L
+// consecutive lanes that hold one 64-column chunk of an output row (fixed shuffle order); the
+// first of them writes the chunk's sum.
+template <typename T, int RS_L>
+__device__ __forceinline__ void rowsq_chunk(const u32x4& v, const GemmArgs& p, int64_t bz,
+                                            int chunk, int row) {
+  const T* e = reinterpret_cast<const T*>(&v);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < (int)(16 / sizeof(T)); ++i) {
+    const float x = (float)e[i];
+    s += x * x;
+  }
+#pragma unroll
+  for (int o = RS_L / 2; o > 0; o >>= 1) s += __shfl_down(s, o, RS_L);
+  if ((threadIdx.x % RS_L) == 0 && row < p.rowsq_rows)
+    p.rowsq[(bz * p.rowsq_chunks + chunk) * p.rowsq_rows + row] = s;
+}
 
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, float* v);
@@ -523,6 +544,8 @@ __global__ __launch_bounds__(256) void k_tail_epilogue(GemmArgs p) {
         for (int e = 0; e < EPC; ++e)
           if (gm <= gn + e) dst[e] = v[e];
       }
+      if (!SYM && p.rowsq)
+        rowsq_chunk<T, CPR>(__builtin_bit_cast(u32x4, v), p, bz, (n0 + sn) / SUB, m0 + gm);
     }
   }
   if (SYM || p.Ct) {
@@ -549,6 +572,8 @@ __global__ __launch_bounds__(256) void k_tail_epilogue(GemmArgs p) {
         for (int e = 0; e < EPC; ++e)
           if (gm + e < gn) dst[e] = vs[e];
       }
+      if (!SYM && p.rowsq && !p.C)
+        rowsq_chunk<T, CPR>(__builtin_bit_cast(u32x4, vs), p, bz, (m0 + sm) / SUB, n0 + gn);
     }
   }
 }
@@ -762,6 +787,9 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   a.M = d.M; a.N = d.N; a.K = d.K;
   a.alpha = d.alpha; a.beta = d.beta; a.gamma = d.gamma;
   a.diag_limit = d.diag_limit;
+  a.rowsq = d.rowsq;
+  a.rowsq_rows = d.rowsq_rows;
+  a.rowsq_chunks = (d.C ? d.N : d.M) / 64;
   a.group = 4;
   if (SYM) {
     const int t = d.M / BM;
@@ -843,6 +871,7 @@ hipError_t gemm(const GemmDesc& d, hipStream_t s) {
   if (d.M % kPad || d.N % kPad || d.K % kPad || d.batch < 1) return hipErrorInvalidValue;
   if (d.sym && (d.M != d.N || !d.C || d.Ct)) return hipErrorInvalidValue;
   if (!d.sym && !d.C && !d.Ct) return hipErrorInvalidValue;
+  if (d.rowsq && (d.sym || d.rowsq_rows < 0)) return hipErrorInvalidValue;
   if (d.elem == Elem::F32) {
     if (tile_for(d) == 64) {
       if (d.sym) return launch<float, 64, 64, 2, 2, true, true>(d, s);

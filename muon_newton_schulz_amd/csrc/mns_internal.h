@@ -60,6 +60,12 @@ struct GemmDesc {
   bool sym = false;
   float* partial = nullptr;    // scratch for split-k partial sums (may be null: no split)
   size_t partial_bytes = 0;
+  // Row sums of squares of the written output (dense products only): the pass that stores C
+  // (C^T when C is null) also writes, for every output row r < rowsq_rows and 64-column chunk
+  // c of that row, rowsq[(b * chunks + c) * rowsq_rows + r] = sum of the squares of the 64
+  // values as stored (chunks = output row length / 64).
+  float* rowsq = nullptr;
+  int rowsq_rows = 0;
 };
 
 // Scratch the GEMM may use for split-k partial sums (part of the caller's workspace).
@@ -104,13 +110,9 @@ hipError_t export_output(const void* X, Elem e, int64_t rows_p, int64_t cols_p, 
                          int64_t rows, int64_t cols, float inv_s, void* O, Store st,
                          hipStream_t s);
 
-// Per stored row i < rows, partial sums of X^2 over 256-wide column chunks:
-//   part[b][chunk][i], chunk < cols_p / 256, X in the stored layout (rows_p x cols_p, pitch
-//   padded_ld(cols_p)).
-hipError_t row_sumsq_x(const void* X, Elem e, int64_t rows_p, int64_t cols_p, int count,
-                       int64_t rows, int64_t cols, float* part, hipStream_t s);
-
-// Same for a caller matrix O (rows x cols, storage st): part[b][0][row].
+// Per row of a caller matrix O (rows x cols, storage st), the sum of its squares:
+// part[b][0][row]. (Inside muon_step the NS result's row sums come from the GEMM epilogue,
+// GemmDesc::rowsq.)
 hipError_t row_sumsq_stored(const void* O, Store st, int count, int64_t rows, int64_t cols,
                             float* part, hipStream_t s);
 

@@ -159,6 +159,15 @@ def test_muon_step_gram_kind(storage):
     _step_case([(260, 1100), (1100, 260)], storage, "gram", (3,), True, 1.0, 10)
 
 
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+def test_normuon_row_sums_from_split_tail(storage):
+    """NorMuon's row statistics come from the epilogue of the product that writes the NS
+    result. At 1024 x 1536 that product's last round of tiles is split along k, so they come
+    from the split-tail epilogue: C's rows for the wide matrix, C^T's for the tall one."""
+    _say("case normuon split tail", storage)
+    _step_case([(1024, 1536), (1536, 1024)], storage, "standard", (), True, 1.0, 40)
+
+
 def test_muon_step_many_matrices_one_shape():
     """More matrices of one shape than one batched launch holds (32: chunking)."""
     _say("case 40 x 128x384")
