@@ -416,6 +416,7 @@ struct StepWs {
   NsBuffers ns;
   float* part = nullptr;
   float* rowscale = nullptr;
+  double* fin = nullptr;
   float* l1 = nullptr;
   int32_t* S = nullptr;
   float* Msel = nullptr;
@@ -432,6 +433,7 @@ size_t carve_step(void* base, const Geo& g, int count, int64_t rows, int64_t col
   w.chunks = (int)(g.cols_p / 64);                     // row-norm partials per stored row
   w.part = cv.take<float>((size_t)count * w.chunks * g.rows);
   w.rowscale = cv.take<float>((size_t)count * g.rows);
+  w.fin = cv.take<double>((size_t)count * 2 * normuon_blocks(g.rows));
   if (dion) {
     w.l1 = cv.take<float>((size_t)count * rows);
     w.S = cv.take<int32_t>((size_t)count * k);
@@ -549,7 +551,7 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
         MNS_HIP(timed("normuon_finalize", 0, 4.0 * c * k * (w.chunks + 3), s, [&] {
           return normuon_finalize(w.part, w.chunks, c, k, cols, &Vp, nullptr, 0,
                                   dion ? w.S : nullptr, hp->beta2, hp->eps, inv_s * inv_s, inv_s,
-                                  w.rowscale, s); }));
+                                  w.rowscale, w.fin, s); }));
       } else {
         MNS_HIP(timed("fill", 0, 4.0 * c * k, s, [&] {
           return fill(w.rowscale, (int64_t)c * k, inv_s, s); }));
@@ -656,12 +658,14 @@ mns_status gram_ns_orthogonalize(const void* X, void* O, int dtype, int64_t batc
 // ---- standalone NorMuon ------------------------------------------------------------------------
 
 static size_t normuon_bytes(int64_t batch, int64_t rows, float** part, float** rowscale,
-                            void* base) {
+                            double** fin, void* base) {
   Carver cv(base);
   float* p = cv.take<float>((size_t)batch * rows);
   float* r = cv.take<float>((size_t)batch * rows);
+  double* f = cv.take<double>((size_t)batch * 2 * normuon_blocks(rows));
   if (part) *part = p;
   if (rowscale) *rowscale = r;
+  if (fin) *fin = f;
   return cv.off + 256;
 }
 
@@ -669,7 +673,7 @@ mns_status mns_normuon_workspace_size(int64_t batch, int64_t rows, int64_t cols,
   if (!bytes) return MNS_ERR_NULL;
   const mns_status st = check_shape(batch, rows, cols);
   if (st != MNS_OK) return st;
-  *bytes = normuon_bytes(batch, rows, nullptr, nullptr, nullptr);
+  *bytes = normuon_bytes(batch, rows, nullptr, nullptr, nullptr, nullptr);
   return MNS_OK;
 }
 
@@ -684,18 +688,20 @@ mns_status normuon_scale(void* O, int dtype, int64_t batch, int64_t rows, int64_
   if (!(beta2 >= 0.f && beta2 <= 1.f) || !(eps >= 0.f) || !std::isfinite(eps)) return MNS_ERR_PARAM;
   if (!aligned(O, 16) || !aligned(v, 4)) return MNS_ERR_PARAM;
   if (batch > 65535) return MNS_ERR_SHAPE;
-  st = check_ws(workspace, workspace_bytes, normuon_bytes(batch, rows, nullptr, nullptr, nullptr));
+  st = check_ws(workspace, workspace_bytes,
+                normuon_bytes(batch, rows, nullptr, nullptr, nullptr, nullptr));
   if (st != MNS_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Store sto = dtype == MNS_BF16 ? Store::BF16 : Store::F32;
   float *part = nullptr, *rowscale = nullptr;
-  normuon_bytes(batch, rows, &part, &rowscale, workspace);
+  double* fin = nullptr;
+  normuon_bytes(batch, rows, &part, &rowscale, &fin, workspace);
   const double all = (double)batch * rows * cols, ss = sto == Store::BF16 ? 2.0 : 4.0;
   MNS_HIP(timed("row_sumsq_stored", 0, all * ss, s, [&] {
     return row_sumsq_stored(O, sto, (int)batch, rows, cols, part, s); }));
   MNS_HIP(timed("normuon_finalize", 0, 4.0 * batch * rows * 4, s, [&] {
     return normuon_finalize(part, 1, (int)batch, rows, cols, nullptr, v, rows, nullptr, beta2,
-                            eps, 1.0f, 1.0f, rowscale, s); }));
+                            eps, 1.0f, 1.0f, rowscale, fin, s); }));
   MNS_HIP(timed("rowscale_apply", 0, 2.0 * all * ss, s, [&] {
     return rowscale_apply(O, sto, (int)batch, rows, cols, rowscale, s); }));
   return MNS_OK;

@@ -358,46 +358,65 @@ __global__ __launch_bounds__(kThreads) void k_row_sumsq_stored(const TO* O, int6
 
 // ---- a7: NorMuon (Eq. 2) v update and the per-row step scale --------------------------------
 
-constexpr int kFinThreads = 1024;
-
-__global__ __launch_bounds__(kFinThreads) void k_normuon_finalize(
+// Stage 1, one thread per row: r_i = inv_s2 * sum over chunks of part, the v update,
+// d_i = 1/(sqrt(v_i) + eps) into rowscale, and per block the float64 sums of r_i and
+// r_i d_i^2 (the squared norms of O and of O-hat) into fin[b][0 / 1][block].
+__global__ __launch_bounds__(kThreads) void k_normuon_rows(
     const float* part, int chunks, int64_t rows, int64_t cols, PtrPack vp, float* v_base,
     int64_t v_stride, const int32_t* rowidx, float beta2, float eps, float inv_s2,
-    float out_scale, float* rowscale) {
-  __shared__ double sh[kFinThreads / 64];
-  __shared__ float ratio_sh;
-  const int b = blockIdx.x;
-  float* v = v_base ? v_base + (int64_t)b * v_stride : static_cast<float*>(vp.p[b]);
-  const float* pt = part + (int64_t)b * chunks * rows;
-  const int32_t* ri = rowidx ? rowidx + (int64_t)b * rows : nullptr;
-  float* rs = rowscale + (int64_t)b * rows;
-  const float inv_cols = 1.0f / (float)cols;
+    float* rowscale, double* fin) {
+  __shared__ double sh[kThreads / 64];
+  const int b = blockIdx.y, nblk = gridDim.x;
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   double s_o = 0.0, s_h = 0.0;
-  for (int64_t i = threadIdx.x; i < rows; i += kFinThreads) {
+  if (i < rows) {
+    float* v = v_base ? v_base + (int64_t)b * v_stride : static_cast<float*>(vp.p[b]);
+    const float* pt = part + (int64_t)b * chunks * rows + i;
     float r4[4] = {0.f, 0.f, 0.f, 0.f};
     int c = 0;
 #pragma unroll 4
     for (; c + 4 <= chunks; c += 4) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) r4[q] += pt[(int64_t)(c + q) * rows + i];
+      for (int q = 0; q < 4; ++q) r4[q] += pt[(int64_t)(c + q) * rows];
     }
-    for (; c < chunks; ++c) r4[0] += pt[(int64_t)c * rows + i];
-    float r = (r4[0] + r4[1]) + (r4[2] + r4[3]);
-    r *= inv_s2;
-    const int64_t vi = ri ? (int64_t)ri[i] : i;
-    const float vn = fmaf(beta2, v[vi], (1.0f - beta2) * (r * inv_cols));
+    for (; c < chunks; ++c) r4[0] += pt[(int64_t)c * rows];
+    const float r = ((r4[0] + r4[1]) + (r4[2] + r4[3])) * inv_s2;
+    const int64_t vi = rowidx ? (int64_t)rowidx[(int64_t)b * rows + i] : i;
+    const float vn = fmaf(beta2, v[vi], (1.0f - beta2) * (r * (1.0f / (float)cols)));
     v[vi] = vn;
     const float d = 1.0f / (sqrtf(vn) + eps);
-    rs[i] = d;
-    s_o += (double)r;
-    s_h += (double)r * (double)d * (double)d;
+    rowscale[(int64_t)b * rows + i] = d;
+    s_o = (double)r;
+    s_h = (double)r * (double)d * (double)d;
   }
-  const double to = block_sum<double, kFinThreads>(s_o, sh);
-  const double th = block_sum<double, kFinThreads>(s_h, sh);
-  if (threadIdx.x == 0) ratio_sh = th > 0.0 ? (float)sqrt(to / th) : 0.f;
+  const double to = block_sum<double, kThreads>(s_o, sh);
+  const double th = block_sum<double, kThreads>(s_h, sh);
+  if (threadIdx.x == 0) {
+    fin[((int64_t)b * 2 + 0) * nblk + blockIdx.x] = to;
+    fin[((int64_t)b * 2 + 1) * nblk + blockIdx.x] = th;
+  }
+}
+
+// Stage 2, one block per matrix: ratio = sqrt(sum r / sum r d^2) = ||O|| / ||O-hat|| from the
+// block sums (0 for a zero matrix), and rowscale_i = ratio * d_i * out_scale.
+__global__ __launch_bounds__(kThreads) void k_normuon_ratio(const double* fin, int nblk,
+                                                            int64_t rows, float out_scale,
+                                                            float* rowscale) {
+  __shared__ double sh[kThreads / 64];
+  __shared__ float scale_sh;
+  const int b = blockIdx.x;
+  double s_o = 0.0, s_h = 0.0;
+  for (int k = threadIdx.x; k < nblk; k += kThreads) {
+    s_o += fin[((int64_t)b * 2 + 0) * nblk + k];
+    s_h += fin[((int64_t)b * 2 + 1) * nblk + k];
+  }
+  const double to = block_sum<double, kThreads>(s_o, sh);
+  const double th = block_sum<double, kThreads>(s_h, sh);
+  if (threadIdx.x == 0) scale_sh = (th > 0.0 ? (float)sqrt(to / th) : 0.f) * out_scale;
   __syncthreads();
-  const float scale = ratio_sh * out_scale;
-  for (int64_t i = threadIdx.x; i < rows; i += kFinThreads) rs[i] = rs[i] * scale;
+  const float scale = scale_sh;
+  float* rs = rowscale + (int64_t)b * rows;
+  for (int64_t i = threadIdx.x; i < rows; i += kThreads) rs[i] = rs[i] * scale;
 }
 
 __global__ __launch_bounds__(kThreads) void k_fill(float* p, int64_t n, float value) {
@@ -764,14 +783,21 @@ hipError_t row_sumsq_stored(const void* O, Store st, int count, int64_t rows, in
   return last();
 }
 
+int normuon_blocks(int64_t rows) { return (int)((rows + kThreads - 1) / kThreads); }
+
 hipError_t normuon_finalize(const float* part, int chunks, int count, int64_t rows, int64_t cols,
                             const PtrPack* v_pack, float* v_base, int64_t v_stride,
                             const int32_t* rowidx, float beta2, float eps, float inv_s2,
-                            float out_scale, float* rowscale, hipStream_t s) {
+                            float out_scale, float* rowscale, double* fin, hipStream_t s) {
   PtrPack vp = {};
   if (v_pack) vp = *v_pack;
-  hipLaunchKernelGGL(k_normuon_finalize, dim3(count), dim3(kFinThreads), 0, s, part, chunks, rows,
-                     cols, vp, v_base, v_stride, rowidx, beta2, eps, inv_s2, out_scale, rowscale);
+  const int nblk = normuon_blocks(rows);
+  hipLaunchKernelGGL(k_normuon_rows, dim3(nblk, count), dim3(kThreads), 0, s, part, chunks, rows,
+                     cols, vp, v_base, v_stride, rowidx, beta2, eps, inv_s2, rowscale, fin);
+  const hipError_t e = last();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_normuon_ratio, dim3(count), dim3(kThreads), 0, s, fin, nblk, rows,
+                     out_scale, rowscale);
   return last();
 }
 

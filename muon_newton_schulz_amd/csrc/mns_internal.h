@@ -119,11 +119,14 @@ hipError_t row_sumsq_stored(const void* O, Store st, int count, int64_t rows, in
 // NorMuon (Eq. 2) per matrix: r_i = inv_s2 * sum_chunk part; v <- beta2 v + (1-beta2) r/cols;
 // d_i = 1/(sqrt(v)+eps); ratio = sqrt(sum r / sum r d^2); rowscale_i = ratio d_i out_scale.
 // rowidx (nullable): v index of row i. v pointers per matrix in the pack (or v_base +
-// b * v_stride when pack is null).
+// b * v_stride when pack is null). fin: scratch of count * 2 * normuon_blocks(rows) doubles
+// (per-block sums of the row-parallel stage).
+int normuon_blocks(int64_t rows);
 hipError_t normuon_finalize(const float* part, int chunks, int count, int64_t rows,
                             int64_t cols, const PtrPack* v_pack, float* v_base,
                             int64_t v_stride, const int32_t* rowidx, float beta2, float eps,
-                            float inv_s2, float out_scale, float* rowscale, hipStream_t s);
+                            float inv_s2, float out_scale, float* rowscale, double* fin,
+                            hipStream_t s);
 
 // rowscale[b][i] = value (plain Muon: every row scaled alike).
 hipError_t fill(float* p, int64_t n, float value, hipStream_t s);
