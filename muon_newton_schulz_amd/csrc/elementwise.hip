@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void k_export(const TX* X, int64_t rows_p
   }
 }
 
-// ---- NorMuon statistics: per stored row, partial sums of O^2 -------------------------------
+// ---- NorMuon statistics of a caller matrix (normuon_scale): per row, the sum of O^2 --------
 
 // Caller-layout O (rows x cols): one block per row, part[b][0][row].
 template <typename TO>
