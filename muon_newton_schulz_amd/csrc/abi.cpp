@@ -418,15 +418,15 @@ struct StepWs {
   float* rowscale = nullptr;
   double* fin = nullptr;
   float* l1 = nullptr;
+  float* l2sq = nullptr;
   int32_t* S = nullptr;
-  float* Msel = nullptr;
   int nblk = 0, chunks = 0;
 };
 
 size_t carve_step(void* base, const Geo& g, int count, int64_t rows, int64_t cols, bool dion,
                   int64_t k, int kind, StepWs& w) {
   Carver cv(base);
-  w.nblk = dion ? (int)k : norm_blocks(rows * cols);
+  w.nblk = dion ? 0 : norm_blocks(rows * cols);
   w.partials = cv.take<float>((size_t)count * w.nblk);
   w.xscale = cv.take<float>((size_t)count);
   carve_ns(cv, g, count, kind, w.ns);
@@ -437,7 +437,7 @@ size_t carve_step(void* base, const Geo& g, int count, int64_t rows, int64_t col
   if (dion) {
     w.l1 = cv.take<float>((size_t)count * rows);
     w.S = cv.take<int32_t>((size_t)count * k);
-    w.Msel = cv.take<float>((size_t)count * k * cols);
+    w.l2sq = cv.take<float>((size_t)count * rows);
   }
   return cv.off + 256;
 }
@@ -525,16 +525,12 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
                            straight(g, w.ns), transposed(g, w.ns), g.rows_p, g.cols_p, s); }));
       } else {
         MNS_HIP(timed("momentum_l1", 0, all * (8.0 + ss), s, [&] {
-          return momentum_l1(Mp, Gp, sto, c, rows, cols, w.l1, s); }));
-        MNS_HIP(timed("topk", 0, 4.0 * c * rows + 4.0 * c * k, s, [&] {
-          return topk_rows(w.l1, c, rows, k, w.S, s); }));
-        MNS_HIP(timed("gather_decay", 0, sel * 12.0, s, [&] {
-          return gather_decay(Mp, c, cols, k, w.S, hp->mu, w.Msel, w.partials, s); }));
-        MNS_HIP(timed("finalize_scale", 0, 4.0 * c * w.nblk, s, [&] {
-          return finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s); }));
-        MNS_HIP(timed("normalize", 0, sel * (4.0 + 2.0 * es), s, [&] {
-          return normalize(nullptr, w.Msel, true, sto, c, k, cols, w.xscale, g.elem,
-                           straight(g, w.ns), transposed(g, w.ns), g.rows_p, g.cols_p, s); }));
+          return momentum_l1(Mp, Gp, sto, c, rows, cols, w.l1, w.l2sq, s); }));
+        MNS_HIP(timed("topk", 0, 8.0 * c * rows + 8.0 * c * k, s, [&] {
+          return topk_rows(w.l1, w.l2sq, c, rows, k, g.S, w.S, w.xscale, s); }));
+        MNS_HIP(timed("gather_normalize", 0, sel * (8.0 + 2.0 * es), s, [&] {
+          return gather_normalize(Mp, c, k, cols, w.S, hp->mu, w.xscale, g.elem,
+                                  straight(g, w.ns), transposed(g, w.ns), g.rows_p, g.cols_p, s); }));
       }
       void* O = nullptr;
       RowSq rs;

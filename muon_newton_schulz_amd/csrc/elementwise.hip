@@ -253,10 +253,13 @@ __global__ __launch_bounds__(kThreads) void k_finalize_scale(const float* partia
 // 16-byte chunks of 8 elements.
 constexpr int kNormRows = 64, kNormCols = 128;
 
-template <typename TS, typename TX>
+// GATHER (Dion3, Algorithm 4): row r of the iterate is source row rowidx[b][r] of the float32
+// momentum, which is also decayed in place (M[S,:] <- mu M[S,:]) from the values just read.
+template <typename TS, typename TX, bool GATHER>
 __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* base, int64_t rows,
                                                         int64_t cols, const float* xscale, TX* S,
-                                                        TX* T, int64_t rows_p, int64_t cols_p) {
+                                                        TX* T, int64_t rows_p, int64_t cols_p,
+                                                        const int32_t* rowidx, float mu) {
   __shared__ float tile[kNormRows][kNormCols + 1];
   const int b = blockIdx.z;
   const TS* s = base ? base + (int64_t)b * rows * cols : static_cast<const TS*>(src.p[b]);
@@ -274,12 +277,24 @@ __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* b
     const int64_t r = r0 + ty + 16 * i;
     v[i] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
     if (r < rows) {
+      const int64_t sr = GATHER ? (int64_t)rowidx[(int64_t)b * rows + r] : r;
       if (vec_ok && c + 8 <= cols) {
-        v[i] = load8<TS>(s, r * cols + c);
+        v[i] = load8<TS>(s, sr * cols + c);
+        if constexpr (GATHER) {
+          const f8 w = v[i];
+          store8<float>(const_cast<float*>(s) + sr * cols, c,
+                        {make_float4(mu * w.lo.x, mu * w.lo.y, mu * w.lo.z, mu * w.lo.w),
+                         make_float4(mu * w.hi.x, mu * w.hi.y, mu * w.hi.z, mu * w.hi.w)});
+        }
       } else {
         float t8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t8[e] = (c + e < cols) ? load1<TS>(s, r * cols + c + e) : 0.f;
+        for (int e = 0; e < 8; ++e) {
+          t8[e] = (c + e < cols) ? load1<TS>(s, sr * cols + c + e) : 0.f;
+          if constexpr (GATHER) {
+            if (c + e < cols) const_cast<float*>(s)[sr * cols + c + e] = mu * t8[e];
+          }
+        }
         v[i] = {make_float4(t8[0], t8[1], t8[2], t8[3]), make_float4(t8[4], t8[5], t8[6], t8[7])};
       }
     }
@@ -501,14 +516,14 @@ __global__ __launch_bounds__(kThreads) void k_rowscale_apply(TO* O, int64_t rows
 
 template <typename TG>
 __global__ __launch_bounds__(kThreads) void k_momentum_l1(PtrPack Mp, PtrPack Gp, int64_t rows,
-                                                          int64_t cols, float* l1) {
+                                                          int64_t cols, float* l1, float* l2sq) {
   __shared__ float sh[kThreads / 64];
   const int b = blockIdx.y;
   float* m = static_cast<float*>(Mp.p[b]);
   const TG* g = static_cast<const TG*>(Gp.p[b]);
   const bool vec_ok = (cols % 4) == 0;
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    float acc = 0.f;
+    float acc = 0.f, acc2 = 0.f;
     if (vec_ok) {
       for (int64_t j = (int64_t)threadIdx.x * 4; j < cols; j += kThreads * 4) {
         float4 mv = load4<float>(m, r * cols + j);
@@ -516,16 +531,22 @@ __global__ __launch_bounds__(kThreads) void k_momentum_l1(PtrPack Mp, PtrPack Gp
         mv.x += gv.x; mv.y += gv.y; mv.z += gv.z; mv.w += gv.w;
         store4<float>(m, r * cols + j, mv);
         acc += fabsf(mv.x) + fabsf(mv.y) + fabsf(mv.z) + fabsf(mv.w);
+        acc2 += mv.x * mv.x + mv.y * mv.y + mv.z * mv.z + mv.w * mv.w;
       }
     } else {
       for (int64_t j = threadIdx.x; j < cols; j += kThreads) {
         const float mv = m[r * cols + j] + load1<TG>(g, r * cols + j);
         m[r * cols + j] = mv;
         acc += fabsf(mv);
+        acc2 += mv * mv;
       }
     }
     const float s = block_sum<float, kThreads>(acc, sh);
-    if (threadIdx.x == 0) l1[(int64_t)b * rows + r] = s;
+    const float s2 = block_sum<float, kThreads>(acc2, sh);
+    if (threadIdx.x == 0) {
+      l1[(int64_t)b * rows + r] = s;
+      l2sq[(int64_t)b * rows + r] = s2;
+    }
   }
 }
 
@@ -573,9 +594,11 @@ __device__ int block_exclusive_scan(int v, int* sh) {
   return res;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, int64_t rows, int64_t k,
-                                                      int32_t* S) {
+__global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, const float* l2sq,
+                                                      int64_t rows, int64_t k, int32_t* S,
+                                                      float Spow, float* xscale) {
   __shared__ uint32_t hist[kSelWaves][256];
+  __shared__ double dsh[kSelWaves];
   __shared__ int scan_sh[kSelThreads];
   __shared__ uint32_t sh_prefix;
   __shared__ int64_t sh_remaining;
@@ -631,54 +654,22 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, int64_t r
   int pos = block_exclusive_scan(sel, scan_sh);
   int e = eq_before;
   int32_t* out = S + (int64_t)b * k;
+  const float* sq = l2sq + (int64_t)b * rows;
+  double ssq = 0.0;
   for (int64_t i = i0; i < i1; ++i) {
     const uint32_t u = order_key(key[i]);
     const bool take = u > prefix || (u == prefix && e++ < remaining);
-    if (take) out[pos++] = (int32_t)i;
+    if (take) {
+      out[pos++] = (int32_t)i;
+      ssq += (double)sq[i];
+    }
   }
+  // ||M[S,:]||_F from the selected rows' sums of squares (fixed order): the normalisation
+  // scale of the selected block (0 for a zero block).
+  const double tot = block_sum<double, kSelThreads>(ssq, dsh);
+  if (t == 0) xscale[b] = tot > 0.0 ? (float)((double)Spow / sqrt(tot)) : 0.f;
 }
 
-__global__ __launch_bounds__(kThreads) void k_gather_decay(PtrPack Mp, int64_t cols, int64_t k,
-                                                           const int32_t* S, float mu, float* Msel,
-                                                           float* partials) {
-  __shared__ float sh[kThreads / 64];
-  const int b = blockIdx.y;
-  float* m = static_cast<float*>(Mp.p[b]);
-  const bool vec_ok = (cols % 4) == 0;
-  for (int64_t p = blockIdx.x; p < k; p += gridDim.x) {
-    const int64_t src = S[(int64_t)b * k + p];
-    float* row = m + src * cols;
-    float* dst = Msel + ((int64_t)b * k + p) * cols;
-    float acc = 0.f;
-    if (vec_ok) {
-      int64_t j = (int64_t)threadIdx.x * 4;
-      for (; j + 4 * kThreads < cols; j += 8 * kThreads) {
-        const float4 v0 = load4<float>(row, j), v1 = load4<float>(row, j + 4 * kThreads);
-        store4<float>(dst, j, v0);
-        store4<float>(dst, j + 4 * kThreads, v1);
-        store4<float>(row, j, make_float4(mu * v0.x, mu * v0.y, mu * v0.z, mu * v0.w));
-        store4<float>(row, j + 4 * kThreads, make_float4(mu * v1.x, mu * v1.y, mu * v1.z, mu * v1.w));
-        acc += v0.x * v0.x + v0.y * v0.y + v0.z * v0.z + v0.w * v0.w;
-        acc += v1.x * v1.x + v1.y * v1.y + v1.z * v1.z + v1.w * v1.w;
-      }
-      if (j < cols) {
-        const float4 v0 = load4<float>(row, j);
-        store4<float>(dst, j, v0);
-        store4<float>(row, j, make_float4(mu * v0.x, mu * v0.y, mu * v0.z, mu * v0.w));
-        acc += v0.x * v0.x + v0.y * v0.y + v0.z * v0.z + v0.w * v0.w;
-      }
-    } else {
-      for (int64_t j = threadIdx.x; j < cols; j += kThreads) {
-        const float v = row[j];
-        dst[j] = v;
-        row[j] = mu * v;
-        acc += v * v;
-      }
-    }
-    const float s = block_sum<float, kThreads>(acc, sh);
-    if (threadIdx.x == 0) partials[(int64_t)b * k + p] = s;
-  }
-}
 
 inline hipError_t last() { return hipGetLastError(); }
 
@@ -725,16 +716,17 @@ hipError_t finalize_scale(const float* partials, int nblk, int count, float S, f
   return last();
 }
 
-template <typename TS, typename TX>
+template <typename TS, typename TX, bool GATHER = false>
 static void launch_normalize(const PtrPack* pack, const void* base, int count, int64_t rows,
                              int64_t cols, const float* xscale, void* S, void* T, int64_t rows_p,
-                             int64_t cols_p, hipStream_t s) {
+                             int64_t cols_p, hipStream_t s, const int32_t* rowidx = nullptr,
+                             float mu = 0.f) {
   PtrPack pk = {};
   if (pack) pk = *pack;
   dim3 grid((unsigned)(cols_p / kNormCols), (unsigned)(rows_p / kNormRows), count);
-  hipLaunchKernelGGL((k_normalize<TS, TX>), grid, dim3(kThreads), 0, s, pk,
+  hipLaunchKernelGGL((k_normalize<TS, TX, GATHER>), grid, dim3(kThreads), 0, s, pk,
                      static_cast<const TS*>(base), rows, cols, xscale, static_cast<TX*>(S),
-                     static_cast<TX*>(T), rows_p, cols_p);
+                     static_cast<TX*>(T), rows_p, cols_p, rowidx, mu);
 }
 
 hipError_t normalize(const PtrPack* pack, const void* base, bool src_f32, Store st, int count,
@@ -847,24 +839,31 @@ hipError_t rowscale_apply(void* O, Store st, int count, int64_t rows, int64_t co
 }
 
 hipError_t momentum_l1(const PtrPack& M, const PtrPack& G, Store g_store, int count, int64_t rows,
-                       int64_t cols, float* l1, hipStream_t s) {
+                       int64_t cols, float* l1, float* l2sq, hipStream_t s) {
   dim3 grid(grid_rows(rows), count);
   if (g_store == Store::BF16)
-    hipLaunchKernelGGL(k_momentum_l1<uint16_t>, grid, dim3(kThreads), 0, s, M, G, rows, cols, l1);
+    hipLaunchKernelGGL(k_momentum_l1<uint16_t>, grid, dim3(kThreads), 0, s, M, G, rows, cols, l1, l2sq);
   else
-    hipLaunchKernelGGL(k_momentum_l1<float>, grid, dim3(kThreads), 0, s, M, G, rows, cols, l1);
+    hipLaunchKernelGGL(k_momentum_l1<float>, grid, dim3(kThreads), 0, s, M, G, rows, cols, l1, l2sq);
   return last();
 }
 
-hipError_t topk_rows(const float* l1, int count, int64_t rows, int64_t k, int32_t* S, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(count), dim3(kSelThreads), 0, s, l1, rows, k, S);
+hipError_t topk_rows(const float* l1, const float* l2sq, int count, int64_t rows, int64_t k,
+                     float Spow, int32_t* S, float* xscale, hipStream_t s) {
+  hipLaunchKernelGGL(k_topk, dim3(count), dim3(kSelThreads), 0, s, l1, l2sq, rows, k, S, Spow,
+                     xscale);
   return last();
 }
 
-hipError_t gather_decay(const PtrPack& M, int count, int64_t cols, int64_t k, const int32_t* S,
-                        float mu, float* Msel, float* partials, hipStream_t s) {
-  dim3 grid(grid_rows(k), count);
-  hipLaunchKernelGGL(k_gather_decay, grid, dim3(kThreads), 0, s, M, cols, k, S, mu, Msel, partials);
+hipError_t gather_normalize(const PtrPack& M, int count, int64_t k, int64_t cols,
+                            const int32_t* S, float mu, const float* xscale, Elem e, void* X,
+                            void* Xt, int64_t rows_p, int64_t cols_p, hipStream_t s) {
+  if (e == Elem::F16)
+    launch_normalize<float, _Float16, true>(&M, nullptr, count, k, cols, xscale, X, Xt, rows_p,
+                                            cols_p, s, S, mu);
+  else
+    launch_normalize<float, float, true>(&M, nullptr, count, k, cols, xscale, X, Xt, rows_p,
+                                         cols_p, s, S, mu);
   return last();
 }
 

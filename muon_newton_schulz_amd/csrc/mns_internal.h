@@ -142,15 +142,17 @@ hipError_t weight_update(const PtrPack& W, Store st, int count, int64_t rows, in
 hipError_t rowscale_apply(void* O, Store st, int count, int64_t rows, int64_t cols,
                           const float* rowscale, hipStream_t s);
 
-// Dion3 (Algorithm 4): M <- M + G with per-row l1 norms of the new M.
+// Dion3 (Algorithm 4): M <- M + G with per-row l1 norms and sums of squares of the new M.
 hipError_t momentum_l1(const PtrPack& M, const PtrPack& G, Store g_store, int count,
-                       int64_t rows, int64_t cols, float* l1, hipStream_t s);
-// S[b][rank] = row for the k rows of largest l1 (ties: lower index first).
-hipError_t topk_rows(const float* l1, int count, int64_t rows, int64_t k, int32_t* S,
-                     hipStream_t s);
-// Msel[b][p][:] = M[S[p]][:]; M[S[p]][:] *= mu; partials[b][p] = sum Msel[p][:]^2.
-hipError_t gather_decay(const PtrPack& M, int count, int64_t cols, int64_t k,
-                        const int32_t* S, float mu, float* Msel, float* partials,
-                        hipStream_t s);
+                       int64_t rows, int64_t cols, float* l1, float* l2sq, hipStream_t s);
+// S[b][rank] = row for the k rows of largest l1 (ties: lower index first), and
+// xscale[b] = Spow / ||M[S,:]||_F from the selected rows' sums of squares (0 for a zero block).
+hipError_t topk_rows(const float* l1, const float* l2sq, int count, int64_t rows, int64_t k,
+                     float Spow, int32_t* S, float* xscale, hipStream_t s);
+// The normalised iterate of the selected rows, like normalize() with row r of the source
+// being M[S[r]] (float32), and in the same pass M[S[r]][:] *= mu.
+hipError_t gather_normalize(const PtrPack& M, int count, int64_t k, int64_t cols,
+                            const int32_t* S, float mu, const float* xscale, Elem e, void* X,
+                            void* Xt, int64_t rows_p, int64_t cols_p, hipStream_t s);
 
 }  // namespace mns
