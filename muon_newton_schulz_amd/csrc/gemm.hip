@@ -33,8 +33,9 @@
 //     k-step, whose fragments are already in registers, so buffer k % 2 is free at that
 //     point and the load of k-tile k+2 starts into it: two k-tiles are in flight with two
 //     buffers, one barrier per k-tile. Each wave's share of a k-tile load (8 DMA
-//     instructions at 256x256) goes out in three parts, one instruction every few MFMAs,
-//     over the last k-step of k-tile k and the first two of k-tile k+1.
+//     instructions at 256x256) goes out in two halves, one instruction after each of the
+//     first MFMAs of the last k-step of k-tile k (just after its barrier) and of the first
+//     k-step of k-tile k+1, so it has most of a k-tile to land before the next barrier.
 //   * MFMA operand roles are swapped (the B tile feeds the MFMA's A input), so each lane's
 //     accumulators hold 4 consecutive output columns of one row.
 //   * The epilogue stages the finished tile in the (then idle) LDS and writes every output
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     const int KL = k_end - k_begin;
     // DMA instruction q of a k-tile (q < A_INST: A row block q, else B row block q - A_INST).
     constexpr int NI = A_INST + B_INST;
-    constexpr int NP0 = (NI + 2) / 3, NP1 = (NI + 1) / 3, NP2 = NI / 3;
+    constexpr int NP0 = NI / 2, NP1 = NI - NP0;
     auto dma_one = [&](int kt, int buf, int q) {
       const int so = kt * BK * ES;
       if (q < A_INST)
@@ -358,10 +359,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     using I0 = std::integral_constant<int, 0>;
     using IP0 = std::integral_constant<int, NP0>;
     using IP1 = std::integral_constant<int, NP1>;
-    using IP2 = std::integral_constant<int, NP2>;
-    // k-tile kl from buffer kl % 2. DMA of k-tile kl+1 (buffer b ^ 1): part 0 went out in the
-    // previous k-tile's last k-step, parts 1 and 2 go out during k-steps 0 and 1 here; the
-    // barrier before k-step 3 waits for it, and part 0 of k-tile kl+2 follows the barrier.
+    // k-tile kl from buffer kl % 2. DMA of k-tile kl+1 (buffer b ^ 1): its first half went
+    // out in the previous k-tile's last k-step, its second half goes out during k-step 0
+    // here; the barrier before k-step 3 waits for it, and the first half of k-tile kl+2
+    // follows the barrier.
     auto body = [&](int kl, auto has1, auto has2) {
       const int b = kl & 1;
       // This k-tile's first fragments were read a whole k-step ago: waiting for them here is
@@ -374,8 +375,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       load_frags(b, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(has1)::value) kstep(1, k_begin + kl + 1, b ^ 1, NP0 + NP1, IP2{});
-      else kstep(1, 0, 0, 0, I0{});
+      kstep(1, 0, 0, 0, I0{});
       __builtin_amdgcn_sched_barrier(0);
       load_frags(b, 3, 1);
       __builtin_amdgcn_sched_barrier(0);
