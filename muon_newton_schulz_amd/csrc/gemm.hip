@@ -771,8 +771,44 @@ __global__ __launch_bounds__(256) void k_gemm_kw(GemmArgs p) {
     }
     return;
   }
-  block_sync();
-  {
+  if constexpr (SYM) {
+    // Symmetric tile: each wave stores its 32 x 32 quarter straight from registers, no LDS
+    // staging and no barrier: the upper triangle (diagonal included) to C as 4-element row
+    // pieces, and its strictly upper part mirrored, where 32 lanes write 32 consecutive
+    // elements of one row of C. The same values and the same triangle rule as the LDS-staged
+    // epilogue.
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const int wm = wave >> 1, wn = wave & 1;
+    const int ml = wm * 32 + (lane & 31);
+    const T* Dg = p.D ? static_cast<const T*>(p.D) + bz * p.sD : nullptr;
+    T* Cg = static_cast<T*>(p.C) + bz * p.sC;
+    const bool diag_tile = tm == tn;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nl = wn * 32 + 8 * g + 4 * (lane >> 5);
+      float d[4] = {0.f, 0.f, 0.f, 0.f};
+      if (Dg) load4<T>(Dg + (int64_t)(m0 + ml) * p.ldd + n0 + nl, d);
+      t4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = p.alpha * acc[0][0][4 * g + e] + p.beta * d[e];
+        if (m0 + ml == n0 + nl + e && m0 + ml < p.diag_limit) v += p.gamma;
+        o[e] = (T)v;
+      }
+      T* dst = Cg + (int64_t)(m0 + ml) * p.ldc + n0 + nl;
+      if (!diag_tile || nl >= ml) {
+        *reinterpret_cast<t4*>(dst) = o;
+      } else if (nl + 3 >= ml) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nl + e >= ml) dst[e] = o[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!diag_tile || ml < nl + e) Cg[(int64_t)(n0 + nl + e) * p.ldc + m0 + ml] = o[e];
+    }
+  } else {
+    block_sync();
     constexpr int WM = 32, WN = 32, FM = 1, FN = 1;   // the 2 x 2 wave layout
     const int wm = wave >> 1, wn = wave & 1;
     T* tile = reinterpret_cast<T*>(&lds[0]);
