@@ -893,12 +893,13 @@ int64_t tiles_of(const GemmDesc& d, int bt) {
   return d.sym ? tm * (tm + 1) / 2 : tm * tn;
 }
 
-// 256 x 256 tiles when they give at least two rounds of blocks over the CUs; 64 x 64 (the
-// k-split kernel) when 128 x 128 tiles would not even fill a quarter of the CUs; else
-// 128 x 128. Float32 uses the same rule without the 256 x 256 step.
+// 256 x 256 tiles when they give at least two rounds of blocks over the CUs, or one round
+// when K is long (>= 4096: the split tail then has k-tiles enough); 64 x 64 (the k-split
+// kernel) when 128 x 128 tiles would not even fill a quarter of the CUs; else 128 x 128.
+// Float32 uses the same rule without the 256 x 256 step.
 int tile_for(const GemmDesc& d) {
   if (d.elem == Elem::F32) return tiles_of(d, 128) * d.batch * 4 < cu_count() ? 64 : 128;
-  if (tiles_of(d, 256) * d.batch >= 2 * cu_count()) return 256;
+  if (tiles_of(d, 256) * d.batch >= (d.K >= 4096 ? 1 : 2) * cu_count()) return 256;
   if (tiles_of(d, 128) * d.batch * 4 < cu_count()) return 64;
   return 128;
 }
