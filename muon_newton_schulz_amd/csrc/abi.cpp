@@ -142,8 +142,13 @@ void carve_ns(Carver& cv, const Geo& g, int count, int kind, NsBuffers& b) {
 
 // Normalisation targets: the stored layout of the source is X for a wide matrix and X^T for
 // a tall one; the other buffer receives the transpose.
-void* straight(const Geo& g, const NsBuffers& b) { return g.tall ? b.Xt[0] : b.X[0]; }
-void* transposed(const Geo& g, const NsBuffers& b) { return g.tall ? b.X[0] : b.Xt[0]; }
+// With km (the products read X k-major) only X is formed: null for the X^T side.
+void* straight(const Geo& g, const NsBuffers& b, bool km) {
+  return g.tall ? (km ? nullptr : b.Xt[0]) : b.X[0];
+}
+void* transposed(const Geo& g, const NsBuffers& b, bool km) {
+  return g.tall ? b.X[0] : (km ? nullptr : b.Xt[0]);
+}
 
 #define MNS_HIP(expr)                               \
   do {                                              \
@@ -178,6 +183,23 @@ GemmDesc left_desc(const Geo& g, int count, const NsBuffers& b, const void* L, c
   return d;
 }
 
+// Whether the products L X of this geometry read the iterate X itself, k-major (float16 on
+// 256 x 256 tiles): X^T is then never formed, except as the stored layout of a tall result.
+bool kmajor_ns(const Geo& g, int count, const NsBuffers& b) {
+  return gemm_kmajor_ok(left_desc(g, count, b, nullptr, nullptr, b.X[1], nullptr));
+}
+
+// L X for the iterate X[cur] (through X^T[cur], or k-major from X[cur] when km).
+GemmDesc lx_desc(const Geo& g, int count, const NsBuffers& b, bool km, const void* L, int cur,
+                 void* C, void* Ct) {
+  GemmDesc d = left_desc(g, count, b, L, b.Xt[cur], C, Ct);
+  if (km) {
+    d.B = b.X[cur]; d.ldb = g.ld_x; d.sB = b.x_stride;
+    d.b_kmajor = true;
+  }
+  return d;
+}
+
 // Optional request for the per-row sums of squares of the NS result (NorMuon's row
 // statistics), taken in the epilogue of the product that writes the result: part gets the
 // GemmDesc::rowsq layout (64-column chunks); done reports whether such a product ran.
@@ -204,14 +226,17 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
   void* B = b.sq[1];
   const float inv_s2 = 1.0f / (g.S * g.S);
   const double nn = (double)count * g.n * g.n;
+  const bool km = kmajor_ns(g, count, b);
   for (int t = 0; t < T; ++t) {
     const float a = abc[3 * t], bb = abc[3 * t + 1], c = abc[3 * t + 2];
     GemmDesc gram = sym_desc(g, count, b, b.X[cur], b.X[cur], g.ld_x, b.x_stride, (int)g.m_p, A);
     gram.alpha = inv_s2;
     MNS_HIP(timed_gemm(gram, nn * g.m, s));
     const bool last = t == T - 1;
-    GemmDesc upd = left_desc(g, count, b, A, b.Xt[cur], (!last || !g.tall) ? b.X[cur ^ 1] : nullptr,
-                             (!last || g.tall) ? b.Xt[cur ^ 1] : nullptr);
+    // X is needed for the next X X^T (and, k-major, the next update); X^T only for the next
+    // update when it cannot read X k-major, and as the stored layout of a tall result.
+    GemmDesc upd = lx_desc(g, count, b, km, A, cur, (!last || !g.tall) ? b.X[cur ^ 1] : nullptr,
+                           (last ? g.tall : !km) ? b.Xt[cur ^ 1] : nullptr);
     if (c != 0.0f) {
       // P = a I + b A + c A^2 (a on the real diagonal only, so padding stays zero), then
       // X <- P X: the same map as a X + (b A + c A^2) X, without re-reading X.
@@ -251,6 +276,7 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
   const float inv_s2 = 1.0f / (g.S * g.S);
   const int n = (int)g.n_p;
   const double nn = (double)count * g.n * g.n;
+  const bool km = kmajor_ns(g, count, b);
 
   GemmDesc gram = sym_desc(g, count, b, b.X[cur], b.X[cur], g.ld_x, b.x_stride, (int)g.m_p, R);
   gram.alpha = inv_s2;
@@ -260,7 +286,8 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
     const float a = abc[3 * (t - 1)], bb = abc[3 * (t - 1) + 1], c = abc[3 * (t - 1) + 2];
     if (t > 1 && ((restart_mask >> t) & 1u)) {
       if (!q_identity) {
-        MNS_HIP(timed_gemm(left_desc(g, count, b, Q, b.Xt[cur], b.X[cur ^ 1], b.Xt[cur ^ 1]),
+        MNS_HIP(timed_gemm(lx_desc(g, count, b, km, Q, cur, b.X[cur ^ 1],
+                                   km ? nullptr : b.Xt[cur ^ 1]),
                            2.0 * nn * g.m, s));
         cur ^= 1;
       }
@@ -292,8 +319,8 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
   if (q_identity) {
     *out = g.tall ? b.Xt[cur] : b.X[cur];
   } else {
-    GemmDesc fin = left_desc(g, count, b, Q, b.Xt[cur], g.tall ? nullptr : b.X[cur ^ 1],
-                             g.tall ? b.Xt[cur ^ 1] : nullptr);
+    GemmDesc fin = lx_desc(g, count, b, km, Q, cur, g.tall ? nullptr : b.X[cur ^ 1],
+                           g.tall ? b.Xt[cur ^ 1] : nullptr);
     want_rowsq(fin, rs);
     MNS_HIP(timed_gemm(fin, 2.0 * nn * g.m, s));
     *out = g.tall ? b.Xt[cur ^ 1] : b.X[cur ^ 1];
@@ -511,6 +538,7 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
       }
       StepWs w;
       carve_step(workspace, g, c, rows, cols, dion, k, hp->kind, w);
+      const bool km = kmajor_ns(g, c, w.ns);
 
       const double all = (double)c * rows * cols;      // elements of the chunk's matrices
       const double sel = (double)c * k * cols;         // elements the NS runs on
@@ -520,17 +548,19 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
           return momentum(Mp, Gp, sto, c, rows * cols, hp->mu, w.partials, s); }));
         MNS_HIP(timed("finalize_scale", 0, 4.0 * c * w.nblk, s, [&] {
           return finalize_scale(w.partials, w.nblk, c, g.S, w.xscale, s); }));
-        MNS_HIP(timed("normalize", 0, all * (4.0 + 2.0 * es), s, [&] {
+        MNS_HIP(timed("normalize", 0, all * (4.0 + (km ? 1.0 : 2.0) * es), s, [&] {
           return normalize(&Mp, nullptr, true, sto, c, rows, cols, w.xscale, g.elem,
-                           straight(g, w.ns), transposed(g, w.ns), g.rows_p, g.cols_p, s); }));
+                           straight(g, w.ns, km), transposed(g, w.ns, km), g.rows_p,
+                           g.cols_p, s); }));
       } else {
         MNS_HIP(timed("momentum_l1", 0, all * (8.0 + ss), s, [&] {
           return momentum_l1(Mp, Gp, sto, c, rows, cols, w.l1, w.l2sq, s); }));
         MNS_HIP(timed("topk", 0, 8.0 * c * rows + 8.0 * c * k, s, [&] {
           return topk_rows(w.l1, w.l2sq, c, rows, k, g.S, w.S, w.xscale, s); }));
-        MNS_HIP(timed("gather_normalize", 0, sel * (8.0 + 2.0 * es), s, [&] {
+        MNS_HIP(timed("gather_normalize", 0, sel * (8.0 + (km ? 1.0 : 2.0) * es), s, [&] {
           return gather_normalize(Mp, c, k, cols, w.S, hp->mu, w.xscale, g.elem,
-                                  straight(g, w.ns), transposed(g, w.ns), g.rows_p, g.cols_p, s); }));
+                                  straight(g, w.ns, km), transposed(g, w.ns, km), g.rows_p,
+                           g.cols_p, s); }));
       }
       void* O = nullptr;
       RowSq rs;
@@ -616,6 +646,7 @@ static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch
     NsBuffers nb;
     float *partials = nullptr, *xscale = nullptr;
     ns_bytes(g, c, kind, rows, cols, &nb, &partials, &xscale, ws);
+    const bool km = kmajor_ns(g, c, nb);
     const char* xin = static_cast<const char*>(X) + (size_t)b0 * rows * cols * esz;
     char* out = static_cast<char*>(O) + (size_t)b0 * rows * cols * esz;
     const double all = (double)c * rows * cols, ss = (double)esz, es = elem_bytes(g.elem);
@@ -624,9 +655,9 @@ static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch
       return sumsq(xin, sto, c, rows * cols, partials, s); }));
     MNS_HIP(timed("finalize_scale", 0, 4.0 * c * nblk, s, [&] {
       return finalize_scale(partials, nblk, c, g.S, xscale, s); }));
-    MNS_HIP(timed("normalize", 0, all * (ss + 2.0 * es), s, [&] {
-      return normalize(nullptr, xin, false, sto, c, rows, cols, xscale, g.elem, straight(g, nb),
-                       transposed(g, nb), g.rows_p, g.cols_p, s); }));
+    MNS_HIP(timed("normalize", 0, all * (ss + (km ? 1.0 : 2.0) * es), s, [&] {
+      return normalize(nullptr, xin, false, sto, c, rows, cols, xscale, g.elem,
+                       straight(g, nb, km), transposed(g, nb, km), g.rows_p, g.cols_p, s); }));
     void* res = nullptr;
     st = run_ns(g, c, nb, kind, T, abc, restart_mask, s, &res);
     if (st != MNS_OK) return st;

@@ -305,11 +305,12 @@ __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* b
     f8 w = v[i];
     w.lo.x *= sc; w.lo.y *= sc; w.lo.z *= sc; w.lo.w *= sc;
     w.hi.x *= sc; w.hi.y *= sc; w.hi.z *= sc; w.hi.w *= sc;
-    store8<TX>(so, (r0 + lr) * lds + c, w);
+    if (S) store8<TX>(so, (r0 + lr) * lds + c, w);
     float* t = &tile[lr][8 * tx];
     t[0] = w.lo.x; t[1] = w.lo.y; t[2] = w.lo.z; t[3] = w.lo.w;
     t[4] = w.hi.x; t[5] = w.hi.y; t[6] = w.hi.z; t[7] = w.hi.w;
   }
+  if (!T) return;   // only the straight layout wanted (the same for every thread)
   __syncthreads();
   // T rows c0 .. c0+kNormCols-1, kNormRows elements (chunks of 8) each
   constexpr int CPT = kNormRows / 8;

@@ -12,10 +12,12 @@
 // symmetric. The a X + (b A + c A^2) X and Z = a I + b R + c R^2 updates use the fused
 // epilogue (alpha, beta * D, gamma * I).
 //
-// Every product is "NT": both operands are row-major with k contiguous. The rectangular
-// products B X and Q X read X through its transposed copy, and their epilogue can write
-// the result in both layouts (C and C^T), which is how the iterate stays available to the
-// next X X^T (rows) and the next B X (columns).
+// Products are "NT" (both operands row-major with k contiguous), except that the dense
+// float16 products on 256 x 256 tiles can take B k-major (B[k][n]): the rectangular
+// products P X and Q X then read the iterate X as it is stored, its k-tiles staged by DMA as
+// 512-byte rows and turned into MFMA fragments by the transposing LDS read
+// (ds_read_b64_tr_b16), and no transposed copy of X is ever written. Elsewhere they read X
+// through its transposed copy, which their epilogue writes beside X (C and C^T).
 //
 // Layout / pipeline:
 //   * WGM x WGN wave64s; block tile BM x BN, wave tile (BM/WGM) x (BN/WGN) of 32 x 32
@@ -180,7 +182,7 @@ __device__ __forceinline__ void load4<float>(const float* p, float* v) {
 
 // The product: whole tiles with their epilogue, and the k-parts of split tiles (float32
 // partial sums, finished by k_tail_epilogue).
-template <typename T, int BM, int BN, int WGM, int WGN, bool SYM>
+template <typename T, int BM, int BN, int WGM, int WGN, bool SYM, bool KB = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   using Tr = Traits<T>;
   constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -191,6 +193,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   constexpr int STAGE = (BM + BN) * kChunks;   // u32x4 per LDS stage
   static_assert(A_INST >= 1 && B_INST >= 1 && FM >= 1 && FN >= 1, "tile too small");
   static_assert(BM * BN * ES <= 2 * STAGE * 16, "epilogue tile must fit the stage buffers");
+  static_assert(!KB || (!SYM && BN == 256 && ES == 2 && WGN == 4 && B_INST == 4),
+                "k-major B: dense float16 256x256 tiles only");
 
   __shared__ u32x4 lds[2 * STAGE];
 
@@ -257,9 +261,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   // Buffer resources based at this block's first A row / B row; reads past the batch slice
   // return zero instead of faulting.
   const char* Abase = static_cast<const char*>(p.A) + (bz * p.sA + (int64_t)m0 * p.lda) * ES;
-  const char* Bbase = static_cast<const char*>(p.B) + (bz * p.sB + (int64_t)n0 * p.ldb) * ES;
+  // k-major B (KB): B[k][n] with row pitch ldb; the block's columns start at n0.
+  const char* Bbase = static_cast<const char*>(p.B) +
+                      (bz * p.sB + (KB ? (int64_t)n0 : (int64_t)n0 * p.ldb)) * ES;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase, ((int64_t)(p.M - m0) * p.lda) * ES);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase, ((int64_t)(p.N - n0) * p.ldb) * ES);
+  const __amdgpu_buffer_rsrc_t rB =
+      make_rsrc(Bbase, (KB ? (int64_t)p.K * p.ldb - n0 : (int64_t)(p.N - n0) * p.ldb) * ES);
 
   // Lane -> (LDS row, physical chunk) of one DMA instruction: row r0 + lane/8, chunk
   // lane%8, which holds logical k-chunk (lane%8) ^ f(row).
@@ -272,10 +279,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   }
 #pragma unroll
   for (int i = 0; i < B_INST; ++i) {
-    const int row = (wave * B_INST + i) * 8 + (lane >> 3);
-    const int ch = (lane & 7) ^ ((row ^ ((row >> 3) & 3)) & 7);
-    offB[i] = (row * (int)p.ldb + ch * VEC) * ES;
+    if constexpr (KB) {
+      // k-major: one instruction fills two 512-byte LDS rows (k-rows 2i', 2i'+1 of the
+      // k-tile); 16-byte chunk c of k-row r sits at c ^ 2 (r % 4), so that a transposing read
+      // (4 k-rows x 32 bytes per 16 lanes) touches 8 distinct chunks.
+      const int kr = 2 * (wave * B_INST + i) + (lane >> 5);
+      const int c = (lane & 31) ^ (2 * (kr & 3));
+      offB[i] = (kr * (int)p.ldb + 8 * c) * ES;
+    } else {
+      const int row = (wave * B_INST + i) * 8 + (lane >> 3);
+      const int ch = (lane & 7) ^ ((row ^ ((row >> 3) & 3)) & 7);
+      offB[i] = (row * (int)p.ldb + ch * VEC) * ES;
+    }
   }
+  // k offset of k-tile kt in the B rows (bytes, scalar)
+  auto b_koff = [&](int kt) { return KB ? kt * BK * (int)p.ldb * ES : kt * BK * ES; };
 
   auto issue = [&](int kt, int buf) {
     const int so = kt * BK * ES;
@@ -284,7 +302,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       dma16(rA, &lds[buf * STAGE + (wave * A_INST + i) * 8 * kChunks], offA[i], so);
 #pragma unroll
     for (int i = 0; i < B_INST; ++i)
-      dma16(rB, &lds[buf * STAGE + (BM + (wave * B_INST + i) * 8) * kChunks], offB[i], so);
+      dma16(rB, &lds[buf * STAGE + (BM + (wave * B_INST + i) * 8) * kChunks], offB[i],
+            b_koff(kt));
   };
 
   floatx16 acc[FM][FN];
@@ -302,8 +321,52 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[slot][i] = lds[buf * STAGE + swz(arow + 32 * i, ch)];
+    if constexpr (!KB) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bf[slot][j] = lds[buf * STAGE + swz(brow + 32 * j, ch)];
+      for (int j = 0; j < FN; ++j) bf[slot][j] = lds[buf * STAGE + swz(brow + 32 * j, ch)];
+    }
+  };
+  // k-major B fragments through ds_read_b64_tr_b16: within each 16-lane group (G = lane / 16)
+  // lane 4s + a points at the 8 bytes of k-row 8 (G / 2) + s (+ 4 for the second read) and
+  // columns n .. n+3, n = wn WN + 32 j + 16 (G % 2) + 4 a; the read hands lane 4a + b the
+  // four k-values of column n + b, so each lane ends with 8 consecutive k of its column --
+  // the fragment the MFMA's A input expects. The loads are inline asm that waits for them
+  // itself (the compiler cannot see that they do not touch the buffer the DMA is filling, and
+  // would otherwise wait for every outstanding DMA first); the outputs are early-clobber and
+  // the fragments the preceding MFMAs read are inputs, so none of those registers is reused
+  // while the MFMAs may still read it.
+  uint32_t b_addr[2] = {0u, 0u};
+  if constexpr (KB) {
+    const uint32_t lbase = (uint32_t)(uintptr_t)(lds_void*)&lds[0];
+    const int G = lane >> 4, sq = (lane & 15) >> 2, a4 = lane & 3;
+    const int kb = 8 * (G >> 1) + sq;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = wn * WN + 32 * j + 16 * (G & 1) + 4 * a4;
+      b_addr[j] = lbase + BM * 128 + kb * 512 + ((n >> 3) ^ (2 * (kb & 3))) * 16 + (n & 7) * 2;
+    }
+  }
+  auto load_b = [&](int buf, int ks, int slot) {
+    if constexpr (KB) {
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      u32x2 t00, t01, t10, t11;
+      const uint32_t o = (uint32_t)(buf * STAGE * 16 + ks * 16 * 512);
+      const uint32_t a0 = b_addr[0] + o, a1 = b_addr[1] + o;
+      const int ps = slot ^ 1;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4\n\t"
+          "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %2, %5\n\t"
+          "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(t00), "=&v"(t01), "=&v"(t10), "=&v"(t11)
+          : "v"(a0), "v"(a1), "v"(af[ps][0]), "v"(af[ps][1]), "v"(af[ps][2]), "v"(af[ps][3]),
+            "v"(bf[ps][0]), "v"(bf[ps][1]));
+      bf[slot][0] = u32x4{t00.x, t00.y, t01.x, t01.y};
+      bf[slot][1] = u32x4{t10.x, t10.y, t11.x, t11.y};
+    } else {
+      (void)buf; (void)ks; (void)slot;
+    }
   };
 
   // Partial sums of a split tile, in fragment order: the float4 (i, j, g) of thread tid,
@@ -326,7 +389,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
         dma16(rA, &lds[buf * STAGE + (wave * A_INST + q) * 8 * kChunks], offA[q], so);
       else
         dma16(rB, &lds[buf * STAGE + (BM + (wave * B_INST + q - A_INST) * 8) * kChunks],
-              offB[q - A_INST], so);
+              offB[q - A_INST], b_koff(kt));
     };
     // One k-step: the MFMAs of fragment slot s with DMA instructions q0 .. q0+nq-1 of k-tile
     // kt spread between them (after every RR-th MFMA).
@@ -373,14 +436,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       if constexpr (decltype(has1)::value) kstep(0, k_begin + kl + 1, b ^ 1, NP0, IP1{});
       else kstep(0, 0, 0, 0, I0{});
       __builtin_amdgcn_sched_barrier(0);
+      load_b(b, 1, 1);
       load_frags(b, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
       kstep(1, 0, 0, 0, I0{});
       __builtin_amdgcn_sched_barrier(0);
+      load_b(b, 2, 0);
       load_frags(b, 3, 1);
       __builtin_amdgcn_sched_barrier(0);
       kstep(0, 0, 0, 0, I0{});
       __builtin_amdgcn_sched_barrier(0);
+      load_b(b, 3, 1);
       // k-tile kl+1 has landed and every wave's reads of buffer b are done.
       block_sync();
       load_frags(b ^ 1, 0, 0);   // after the last k-tile: a harmless read of the idle buffer
@@ -388,6 +454,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       if constexpr (decltype(has2)::value) kstep(1, k_begin + kl + 2, b, 0, IP0{});
       else kstep(1, 0, 0, 0, I0{});
       __builtin_amdgcn_sched_barrier(0);
+      load_b(b ^ 1, 0, 0);   // after the last k-tile: a harmless read of the idle buffer
     };
     using T1 = std::true_type;
     using F1 = std::false_type;
@@ -398,6 +465,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     }
     block_sync();
     load_frags(0, 0, 0);
+    load_b(0, 0, 0);
     int kl = 0;
     for (; kl + 2 < KL; ++kl) body(kl, T1{}, T1{});
     if (kl + 1 < KL) body(kl++, T1{}, F1{});
@@ -816,7 +884,8 @@ __global__ __launch_bounds__(256) void k_gemm_kw(GemmArgs p) {
   }
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, bool SYM, bool KW = false>
+template <typename T, int BM, int BN, int WGM, int WGN, bool SYM, bool KW = false,
+          bool KB = false>
 hipError_t launch(const GemmDesc& d, hipStream_t s) {
   GemmArgs a;
   a.A = d.A; a.B = d.B; a.D = d.D; a.C = d.C; a.Ct = d.Ct;
@@ -860,7 +929,7 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   if constexpr (KW)
     hipLaunchKernelGGL((k_gemm_kw<T, SYM>), dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM>), dim3(blocks), dim3(64 * WGM * WGN), 0,
+    hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, SYM, KB>), dim3(blocks), dim3(64 * WGM * WGN), 0,
                        s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split < 2) return e;
@@ -911,6 +980,10 @@ hipError_t gemm(const GemmDesc& d, hipStream_t s) {
   if (d.sym && (d.M != d.N || !d.C || d.Ct)) return hipErrorInvalidValue;
   if (!d.sym && !d.C && !d.Ct) return hipErrorInvalidValue;
   if (d.rowsq && (d.sym || d.rowsq_rows < 0)) return hipErrorInvalidValue;
+  if (d.b_kmajor) {
+    if (!gemm_kmajor_ok(d)) return hipErrorInvalidValue;
+    return launch<_Float16, 256, 256, 2, 4, false, false, true>(d, s);
+  }
   if (d.elem == Elem::F32) {
     if (tile_for(d) == 64) {
       if (d.sym) return launch<float, 64, 64, 2, 2, true, true>(d, s);
@@ -925,6 +998,10 @@ hipError_t gemm(const GemmDesc& d, hipStream_t s) {
     return launch<_Float16, 64, 64, 2, 2, false, true>(d, s);
   }
   return dispatch_tile<_Float16, 128, 2, 2>(d, s);
+}
+
+bool gemm_kmajor_ok(const GemmDesc& d) {
+  return d.elem == Elem::F16 && !d.sym && tile_for(d) == 256;
 }
 
 const char* gemm_name(const GemmDesc& d) {

@@ -66,6 +66,10 @@ struct GemmDesc {
   // values as stored (chunks = output row length / 64).
   float* rowsq = nullptr;
   int rowsq_rows = 0;
+  // B given k-major: B[k][n] (K x N, row pitch ldb) instead of B[n][k] -- the iterate X read
+  // as it is stored, so no transposed copy is needed. Dense float16 products on 256 x 256
+  // tiles only (gemm_kmajor_ok).
+  bool b_kmajor = false;
 };
 
 // Scratch the GEMM may use for split-k partial sums (part of the caller's workspace).
@@ -73,6 +77,8 @@ constexpr size_t kGemmScratchBytes = size_t(64) << 20;
 hipError_t gemm(const GemmDesc& d, hipStream_t s);
 // Name of the kernel instantiation gemm() launches for this descriptor.
 const char* gemm_name(const GemmDesc& d);
+// Whether gemm() can take this (dense) product's B operand k-major (GemmDesc::b_kmajor).
+bool gemm_kmajor_ok(const GemmDesc& d);
 
 // ---------------------------------------------------------------------------------------
 // Elementwise / reduction kernels (elementwise.hip). All are deterministic: fixed
@@ -99,7 +105,8 @@ hipError_t finalize_scale(const float* partials, int nblk, int count, float S, f
 // padded_ld(cols_p)) = xscale * src and T (cols_p x rows_p, pitch padded_ld(rows_p)) = its
 // transpose; src is rows x cols (float32 when src_f32, else storage `st`). src pointers: a
 // pack (per matrix) or, when pack == nullptr, base + b * rows * cols. Outputs are batched
-// with stride rows_p * padded_ld(cols_p) and cols_p * padded_ld(rows_p).
+// with stride rows_p * padded_ld(cols_p) and cols_p * padded_ld(rows_p). S or T may be null:
+// that layout is not written.
 hipError_t normalize(const PtrPack* pack, const void* base, bool src_f32, Store st, int count,
                      int64_t rows, int64_t cols, const float* xscale, Elem e, void* S, void* T,
                      int64_t rows_p, int64_t cols_p, hipStream_t s);
