@@ -193,8 +193,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   constexpr int STAGE = (BM + BN) * kChunks;   // u32x4 per LDS stage
   static_assert(A_INST >= 1 && B_INST >= 1 && FM >= 1 && FN >= 1, "tile too small");
   static_assert(BM * BN * ES <= 2 * STAGE * 16, "epilogue tile must fit the stage buffers");
-  static_assert(!KB || (!SYM && BN == 256 && ES == 2 && WGN == 4 && B_INST == 4),
-                "k-major B: dense float16 256x256 tiles only");
+  static_assert(!KB || (!SYM && (BN == 256 || BN == 128) && ES == 2 && WN == 64 && FN == 2),
+                "k-major B: dense float16 tiles of 256 or 128 columns, 64-column wave tiles");
+  // k-major B: a k-row of the tile is BN * 2 bytes (KCH 16-byte chunks); one DMA instruction
+  // (1 KB) fills KRI k-rows.
+  constexpr int KCH = BN / 8, KRI = 64 / KCH, KRB = BN * 2;
 
   __shared__ u32x4 lds[2 * STAGE];
 
@@ -280,11 +283,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < B_INST; ++i) {
     if constexpr (KB) {
-      // k-major: one instruction fills two 512-byte LDS rows (k-rows 2i', 2i'+1 of the
-      // k-tile); 16-byte chunk c of k-row r sits at c ^ 2 (r % 4), so that a transposing read
-      // (4 k-rows x 32 bytes per 16 lanes) touches 8 distinct chunks.
-      const int kr = 2 * (wave * B_INST + i) + (lane >> 5);
-      const int c = (lane & 31) ^ (2 * (kr & 3));
+      // k-major: one instruction fills KRI k-rows of the tile; 16-byte chunk c of k-row r sits
+      // at c ^ 2 (r % 4), so that a transposing read (4 k-rows x 32 bytes per 16 lanes)
+      // touches 8 distinct chunks.
+      const int kr = KRI * (wave * B_INST + i) + lane / KCH;
+      const int c = (lane % KCH) ^ (2 * (kr & 3));
       offB[i] = (kr * (int)p.ldb + 8 * c) * ES;
     } else {
       const int row = (wave * B_INST + i) * 8 + (lane >> 3);
@@ -343,25 +346,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = wn * WN + 32 * j + 16 * (G & 1) + 4 * a4;
-      b_addr[j] = lbase + BM * 128 + kb * 512 + ((n >> 3) ^ (2 * (kb & 3))) * 16 + (n & 7) * 2;
+      b_addr[j] = lbase + BM * 128 + kb * KRB + ((n >> 3) ^ (2 * (kb & 3))) * 16 + (n & 7) * 2;
     }
   }
   auto load_b = [&](int buf, int ks, int slot) {
     if constexpr (KB) {
       typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
       u32x2 t00, t01, t10, t11;
-      const uint32_t o = (uint32_t)(buf * STAGE * 16 + ks * 16 * 512);
+      const uint32_t o = (uint32_t)(buf * STAGE * 16 + ks * 16 * KRB);
       const uint32_t a0 = b_addr[0] + o, a1 = b_addr[1] + o;
       const int ps = slot ^ 1;
+      // the second read of each pair is 4 k-rows further (offset 4 KRB)
+      static_assert(FM == 4 || FM == 2, "fragment inputs below");
+      const u32x4 pa2 = af[ps][FM > 2 ? 2 : 0], pa3 = af[ps][FM > 2 ? 3 : 1];
       asm volatile(
           "ds_read_b64_tr_b16 %0, %4\n\t"
-          "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %1, %4 offset:%c12\n\t"
           "ds_read_b64_tr_b16 %2, %5\n\t"
-          "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %3, %5 offset:%c12\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(t00), "=&v"(t01), "=&v"(t10), "=&v"(t11)
-          : "v"(a0), "v"(a1), "v"(af[ps][0]), "v"(af[ps][1]), "v"(af[ps][2]), "v"(af[ps][3]),
-            "v"(bf[ps][0]), "v"(bf[ps][1]));
+          : "v"(a0), "v"(a1), "v"(af[ps][0]), "v"(af[ps][1]), "v"(pa2), "v"(pa3),
+            "v"(bf[ps][0]), "v"(bf[ps][1]), "i"(4 * KRB));
       bf[slot][0] = u32x4{t00.x, t00.y, t01.x, t01.y};
       bf[slot][1] = u32x4{t10.x, t10.y, t11.x, t11.y};
     } else {
@@ -982,7 +988,8 @@ hipError_t gemm(const GemmDesc& d, hipStream_t s) {
   if (d.rowsq && (d.sym || d.rowsq_rows < 0)) return hipErrorInvalidValue;
   if (d.b_kmajor) {
     if (!gemm_kmajor_ok(d)) return hipErrorInvalidValue;
-    return launch<_Float16, 256, 256, 2, 4, false, false, true>(d, s);
+    if (tile_for(d) == 256) return launch<_Float16, 256, 256, 2, 4, false, false, true>(d, s);
+    return launch<_Float16, 128, 128, 2, 2, false, false, true>(d, s);
   }
   if (d.elem == Elem::F32) {
     if (tile_for(d) == 64) {
@@ -1001,7 +1008,9 @@ hipError_t gemm(const GemmDesc& d, hipStream_t s) {
 }
 
 bool gemm_kmajor_ok(const GemmDesc& d) {
-  return d.elem == Elem::F16 && !d.sym && tile_for(d) == 256;
+  if (d.elem != Elem::F16 || d.sym) return false;
+  const int bt = tile_for(d);
+  return bt == 256 || bt == 128;
 }
 
 const char* gemm_name(const GemmDesc& d) {

@@ -67,8 +67,8 @@ struct GemmDesc {
   float* rowsq = nullptr;
   int rowsq_rows = 0;
   // B given k-major: B[k][n] (K x N, row pitch ldb) instead of B[n][k] -- the iterate X read
-  // as it is stored, so no transposed copy is needed. Dense float16 products on 256 x 256
-  // tiles only (gemm_kmajor_ok).
+  // as it is stored, so no transposed copy is needed. Dense float16 products on 256 x 256 or
+  // 128 x 128 tiles only (gemm_kmajor_ok).
   bool b_kmajor = false;
 };
 
