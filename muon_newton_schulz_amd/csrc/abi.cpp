@@ -110,8 +110,10 @@ Geo make_geo(int64_t rows, int64_t cols, Store st) {
   return g;
 }
 
-// The iterate is kept in two layouts: X (n_p x m_p, rows = the short side) feeds X X^T and
-// X^T (m_p x n_p) feeds the k-contiguous operand of B X and Q X; each has a ping-pong pair.
+// The iterate X (n_p x m_p, rows = the short side) feeds X X^T and, read k-major, B X and
+// Q X; its transposed copy X^T (m_p x n_p) is formed only where those products cannot read X
+// k-major (64 x 64 tiles, float32) and as the stored layout of a tall result. Each layout
+// has a ping-pong pair.
 struct NsBuffers {
   void* X[2] = {};
   void* Xt[2] = {};
@@ -184,7 +186,8 @@ GemmDesc left_desc(const Geo& g, int count, const NsBuffers& b, const void* L, c
 }
 
 // Whether the products L X of this geometry read the iterate X itself, k-major (float16 on
-// 256 x 256 tiles): X^T is then never formed, except as the stored layout of a tall result.
+// 256 x 256 or 128 x 128 tiles): X^T is then never formed, except as the stored layout of a
+// tall result.
 bool kmajor_ns(const Geo& g, int count, const NsBuffers& b) {
   return gemm_kmajor_ok(left_desc(g, count, b, nullptr, nullptr, b.X[1], nullptr));
 }

@@ -13,9 +13,10 @@
 // epilogue (alpha, beta * D, gamma * I).
 //
 // Products are "NT" (both operands row-major with k contiguous), except that the dense
-// float16 products on 256 x 256 tiles can take B k-major (B[k][n]): the rectangular
-// products P X and Q X then read the iterate X as it is stored, its k-tiles staged by DMA as
-// 512-byte rows and turned into MFMA fragments by the transposing LDS read
+// float16 products on 256 x 256 and 128 x 128 tiles can take B k-major (B[k][n]): the
+// rectangular products P X and Q X then read the iterate X as it is stored, its k-tiles
+// staged by DMA as 512- or 256-byte rows and turned into MFMA fragments by the transposing
+// LDS read
 // (ds_read_b64_tr_b16), and no transposed copy of X is ever written. Elsewhere they read X
 // through its transposed copy, which their epilogue writes beside X (C and C^T).
 //
