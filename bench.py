@@ -207,7 +207,7 @@ def main():
     import muon_newton_schulz_amd as mns
     import synthetic
 
-    wl = synthetic.CONFIGS[args.config]
+    wl = synthetic.WORKLOADS[args.config]
     kind = args.kind or wl.kind
     restarts = wl.restart_before if kind == "gram" else ()
     if kind == "gram" and not restarts:

@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .configs import CONFIGS, Workload, MatrixSpec  # noqa: F401
+from .configs import WORKLOADS, Workload, MatrixSpec  # noqa: F401
 
 _TAG_GRAD = 0x6D6E73          # distinct streams for gradients, weights and states
 _TAG_WEIGHT = 0x77

@@ -60,7 +60,7 @@ class Workload:
         return [self.coeffs] * self.T
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload(1, "fp32 256x1024 single matrix", "f32", (MatrixSpec(256, 1024),), "normal",
                 steps=1),
     2: Workload(2, "4 x 4096x4096 bf16 (attention-like)", "bf16", (MatrixSpec(4096, 4096, 4),),

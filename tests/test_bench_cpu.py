@@ -23,7 +23,7 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_build_inputs_matches_workload():
-    wl = synthetic.CONFIGS[1]
+    wl = synthetic.WORKLOADS[1]
     W, M, G, V = bench.build_inputs(wl, torch, np, synthetic, torch.device("cpu"))
     assert len(W) == len(M) == len(G) == len(V) == wl.n_matrices
     for (idx, r, c), w, m, g, v in zip(wl.matrices(), W, M, G, V):
@@ -35,7 +35,7 @@ def test_build_inputs_matches_workload():
 
 def test_build_inputs_bf16_bits_preserved():
     # a bf16 workload cut to two small matrices: the device copies keep the gradient's bits
-    wl = dataclasses.replace(synthetic.CONFIGS[2], groups=(synthetic.configs.MatrixSpec(64, 192, 2),))
+    wl = dataclasses.replace(synthetic.WORKLOADS[2], groups=(synthetic.configs.MatrixSpec(64, 192, 2),))
     W, M, G, V = bench.build_inputs(wl, torch, np, synthetic, torch.device("cpu"))
     for (idx, r, c), w, g in zip(wl.matrices(), W, G):
         assert g.dtype == torch.bfloat16 and w.dtype == torch.bfloat16

@@ -37,7 +37,7 @@ def _oracle_kw(wl, kind=None):
 
 @pytest.mark.timeout(300)
 def test_config1_fp32_256x1024():
-    wl = synthetic.CONFIGS[1]
+    wl = synthetic.WORKLOADS[1]
     _say("config 1:", wl.name)
     g = synthetic.gradient(wl.dist, 256, 1024, "f32", 1, 0, 0)
     W = torch.zeros(256, 1024, device="cuda")
@@ -60,7 +60,7 @@ def test_config1_fp32_256x1024():
 
 @pytest.mark.timeout(600)
 def test_config2_4x4096_bf16_two_steps():
-    wl = synthetic.CONFIGS[2]
+    wl = synthetic.WORKLOADS[2]
     _say("config 2:", wl.name)
     shape = (4096, 4096)
     W = [torch.zeros(*shape, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
@@ -83,7 +83,7 @@ def test_config2_4x4096_bf16_two_steps():
 
 @pytest.mark.timeout(600)
 def test_config3_4096x16384_standard_and_gram():
-    wl = synthetic.CONFIGS[3]
+    wl = synthetic.WORKLOADS[3]
     _say("config 3:", wl.name)
     g = synthetic.gradient(wl.dist, 4096, 16384, "bf16", 3, 0, 0)
     G = to_device(g, "bf16")
@@ -108,7 +108,7 @@ def test_config3_4096x16384_standard_and_gram():
 
 @pytest.mark.timeout(900)
 def test_config4_layer_set_grouped():
-    wl = synthetic.CONFIGS[4]
+    wl = synthetic.WORKLOADS[4]
     _say("config 4:", wl.name)
     mats = wl.matrices()
     W, M, G, V, Gs = [], [], [], [], {}
@@ -149,7 +149,7 @@ def test_config4_layer_set_grouped():
 
 @pytest.mark.timeout(900)
 def test_config5_dion3_ten_steps_resynced():
-    wl = synthetic.CONFIGS[5]
+    wl = synthetic.WORKLOADS[5]
     _say("config 5:", wl.name)
     rows, cols = 5120, 13824
     k = oracle.rows_for_fraction(wl.row_fraction, rows)
@@ -186,7 +186,7 @@ def test_config5_dion3_ten_steps_resynced():
 
 @pytest.mark.timeout(900)
 def test_config6_moe_alpha8_gram_and_standard():
-    wl = synthetic.CONFIGS[6]
+    wl = synthetic.WORKLOADS[6]
     _say("config 6:", wl.name)
     mats = wl.matrices()
     G64, Gd = {}, []
@@ -219,7 +219,7 @@ def test_config6_moe_alpha8_gram_and_standard():
 
 @pytest.mark.timeout(900)
 def test_config7_coefficient_schedule():
-    wl = synthetic.CONFIGS[7]
+    wl = synthetic.WORKLOADS[7]
     _say("config 7:", wl.name)
     sched = wl.coeff_table()
     mats = wl.matrices()

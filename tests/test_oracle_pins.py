@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synthetic
-from synthetic import CONFIGS
+from synthetic import WORKLOADS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -164,7 +164,7 @@ def test_coefficient_schedule_reaches_polar(shape, seed):
     schedule stays ~0.2 away: its fixed point is not 1)."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal(shape)
-    sched = CONFIGS[7].coeff_table()
+    sched = WORKLOADS[7].coeff_table()
     out = oracle.newton_schulz(x, sched)
     assert _rel(out, _closed_form(x, sched)) < 1e-12
     assert _rel(out, oracle.polar_svd(x)) < 1e-3
@@ -397,7 +397,7 @@ def test_lr_transfer_rule_matches_norms():
     full = np.linalg.norm(lr * oracle.polar_svd(M))
     part = np.linalg.norm(oracle.transfer_lr(lr, f) * oracle.polar_svd(M[S]))
     assert abs(full - lr * math.sqrt(n)) < 1e-14 and abs(part - full) < 1e-14
-    assert abs(oracle.transfer_lr(0.02, CONFIGS[5].row_fraction) - CONFIGS[5].lr) < 1e-15
+    assert abs(oracle.transfer_lr(0.02, WORKLOADS[5].row_fraction) - WORKLOADS[5].lr) < 1e-15
 
 
 def test_dion3_uses_given_rows():
