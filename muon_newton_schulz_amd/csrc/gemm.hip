@@ -285,10 +285,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   for (int i = 0; i < B_INST; ++i) {
     if constexpr (KB) {
       // k-major: one instruction fills KRI k-rows of the tile; 16-byte chunk c of k-row r sits
-      // at c ^ 2 (r % 4), so that a transposing read (4 k-rows x 32 bytes per 16 lanes)
-      // touches 8 distinct chunks.
+      // at c ^ 4 (r % 4), so that a transposing read (4 k-rows x 64 bytes per 32 lanes)
+      // touches 16 distinct chunk positions, i.e. all 64 banks once.
       const int kr = KRI * (wave * B_INST + i) + lane / KCH;
-      const int c = (lane % KCH) ^ (2 * (kr & 3));
+      const int c = (lane % KCH) ^ (4 * (kr & 3));
       offB[i] = (kr * (int)p.ldb + 8 * c) * ES;
     } else {
       const int row = (wave * B_INST + i) * 8 + (lane >> 3);
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = wn * WN + 32 * j + 16 * (G & 1) + 4 * a4;
-      b_addr[j] = lbase + BM * 128 + kb * KRB + ((n >> 3) ^ (2 * (kb & 3))) * 16 + (n & 7) * 2;
+      b_addr[j] = lbase + BM * 128 + kb * KRB + ((n >> 3) ^ (4 * (kb & 3))) * 16 + (n & 7) * 2;
     }
   }
   auto load_b = [&](int buf, int ks, int slot) {
