@@ -2,12 +2,22 @@
 """Benchmark of the Muon / Newton-Schulz optimizer step on one MI355X.
 
 A step is one muon_step call over a workload's matrices (momentum, normalisation, T
-Newton-Schulz iterations, NorMuon and the weight update), inputs resident in HBM.
-Prints one JSON line: NS algorithmic TFLOP/s over the whole step, step ms, the dominant
-kernel's roofline (from hipEvents the library records around its launches during the timed
-steps), a per-kernel breakdown, and the fp64 oracle timed on a bounded sample on the host.
+Newton-Schulz iterations, NorMuon and the weight update), inputs resident in HBM. The
+default workload is the largest: the 196-matrix layer set of a 3B-like transformer
+(28 x {4 x 3072^2, 2 x 3072x8192, 1 x 8192x3072} bf16, NorMuon). Prints one JSON line:
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {1..7}] [--kind standard|gram]
+  * value: NS algorithmic TFLOP/s over the whole step (symmetric products priced at half the
+    dense 2MNK); ms_per_step over the timed steps; the dense-equivalent rate beside it;
+  * roofline: the dominant kernel's algorithmic FLOPs per launch over its mean launch time,
+    from hipEvents the library records around each of its launches during the timed steps;
+  * kernels: per-kernel breakdown of the timed steps;
+  * hbm_kernels_cache_flushed: the elementwise / reduction kernels timed again with a 1 GiB
+    buffer written before each launch (the 256 MB Infinity Cache evicted);
+  * ns_gate_4096x16384: the 4096x16384 bf16 standard-NS step timed in the same process, its
+    Newton-Schulz GEMM phase as a fraction of the bf16 MFMA peak;
+  * cpu_baseline: the fp64 oracle on a bounded sample, on the host's cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {1..7}] [--kind standard|gram]
 """
 from __future__ import annotations
 
@@ -24,34 +34,55 @@ if ROOT not in sys.path:
 # MI355X published peaks (dense MFMA and HBM3E)
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = 4          # the 196-matrix layer set (the largest workload)
+GATE_WORKLOAD = 3             # 4096x16384 bf16, standard NS: the MFMA gate (>= 60 % of peak)
+MFMA_GATE = 0.60
+HBM_GATE = 0.70
+FLUSH_BYTES = 1 << 30
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", "--config", dest="workload", type=int, default=DEFAULT_WORKLOAD,
+                    choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--kind", choices=["standard", "gram"], default=None,
                     help="override the workload's Newton-Schulz variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
-    ap.add_argument("--graph", action="store_true",
-                    help="(default) also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP graph replay timing")
+    ap.add_argument("--no-gate", action="store_true",
+                    help="skip the 4096x16384 standard-NS gate timing")
+    ap.add_argument("--no-flush-pass", action="store_true",
+                    help="skip the cache-flushed timing of the HBM kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
+
+
+def gradient_bits(wl, synthetic, threads: int = 8):
+    """The workload's seeded gradients (stored bits), drawn on `threads` host threads (the
+    generators release the GIL); the same bits as synthetic.gradient one by one."""
+    from concurrent.futures import ThreadPoolExecutor
+    mats = wl.matrices()
+
+    def one(m):
+        idx, rows, cols = m
+        return synthetic.gradient(wl.dist, rows, cols, wl.storage, wl.index, 0, idx)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        yield from ex.map(one, mats)
 
 
 def build_inputs(wl, torch, np, synthetic, dev):
     """The workload's matrices, resident on `dev`: seeded synthetic gradients, zero weights,
     momenta and second-moment vectors."""
     W, M, G, V = [], [], [], []
-    for idx, rows, cols in wl.matrices():
-        g = synthetic.gradient(wl.dist, rows, cols, wl.storage, wl.index, 0, idx)
+    for (idx, rows, cols), g in zip(wl.matrices(), gradient_bits(wl, synthetic)):
         if wl.storage == "bf16":
             G.append(torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).to(dev))
             W.append(torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev))
@@ -61,6 +92,24 @@ def build_inputs(wl, torch, np, synthetic, dev):
         M.append(torch.zeros(rows, cols, dtype=torch.float32, device=dev))
         V.append(torch.zeros(rows, dtype=torch.float32, device=dev))
     return W, M, G, V
+
+
+def ns_shapes(wl):
+    """(n, m) of the Newton-Schulz problem of every matrix: n the short side (the selected
+    rows under Dion3), m the long side."""
+    import math
+    out = []
+    for _, rows, cols in wl.matrices():
+        if wl.row_fraction < 1.0:
+            rows = max(1, min(rows, math.ceil(wl.row_fraction * rows)))
+        out.append((min(rows, cols), max(rows, cols)))
+    return out
+
+
+def dense_equivalent_flops(wl) -> float:
+    """FLOPs of standard NS with every product computed dense, T (4 m n^2 + 2 n^3) per matrix
+    (the dense count the page's FLOP analysis starts from)."""
+    return float(sum(wl.T * (4 * m * n * n + 2 * n ** 3) for n, m in ns_shapes(wl)))
 
 
 GEMM_SOURCES = [os.path.join(ROOT, "muon_newton_schulz_amd", "csrc", f)
@@ -112,21 +161,46 @@ def calibrate_copy():
                       "bytes_written_per_launch": 4 * n, "launches": 3}), flush=True)
 
 
+def host_info():
+    """Host CPU model, logical CPUs, and the BLAS library the oracle's NumPy uses."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = [], None
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas.append({k: i.get(k) for k in ("internal_api", "version", "num_threads",
+                                                    "threading_layer", "architecture")})
+                threads = max(threads or 0, int(i.get("num_threads") or 0))
+    except Exception:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity,
+            "blas": blas}, threads
+
+
 def cpu_baseline(wl, kind, budget_s):
     """The fp64 oracle as it stands, timed on a bounded sample of the workload: the full
     Newton-Schulz orthogonalisation of the workload's matrices in order (starting over after
     the last), as many as fit the budget (at least the first; only its first iteration when
-    even one full orthogonalisation would overrun the budget). Returns the oracle's algorithmic TFLOP/s (the same FLOP
-    accounting as the GPU value)."""
+    even one full orthogonalisation would overrun the budget). Returns the oracle's
+    algorithmic TFLOP/s (the same FLOP accounting as the GPU value)."""
     import numpy as np
     import oracle
     import synthetic
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
+    info, threads = host_info()
+    threads = threads or os.cpu_count() or 1
     coeffs = wl.coeff_table()
     restarts = (wl.restart_before or (3,)) if kind == "gram" else ()
 
@@ -151,7 +225,7 @@ def cpu_baseline(wl, kind, budget_s):
                 "kind": "oracle",
                 "sample": f"{kind} NS of matrix 0 ({x.shape[0]}x{x.shape[1]}) of "
                           f"{wl.n_matrices}, 1 of {len(coeffs)} iterations, fp64 NumPy, "
-                          f"{dt:.1f} s"}
+                          f"{dt:.1f} s", **info}
     # The workload's matrices in order, starting over after the last one, until one more
     # orthogonalisation would overrun the budget.
     flops, dt, done, last = 0, 0.0, 0, 0.0
@@ -168,7 +242,7 @@ def cpu_baseline(wl, kind, budget_s):
             "kind": "oracle",
             "sample": f"{kind} NS ({len(coeffs)} iterations) of {done} matrices taken in order "
                       f"from the workload's {wl.n_matrices} (cycling; operand "
-                      f"{x.shape[0]}x{x.shape[1]} first), fp64 NumPy, {dt:.1f} s"}
+                      f"{x.shape[0]}x{x.shape[1]} first), fp64 NumPy, {dt:.1f} s", **info}
 
 
 def graph_timing(mns, torch, step_args, ws, kw, warmup, steps):
@@ -188,11 +262,80 @@ def graph_timing(mns, torch, step_args, ws, kw, warmup, steps):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
+    del g
     return {"ms_per_step": round(e0.elapsed_time(e1) / steps, 4), "steps": steps}
 
 
-def main():
-    args = parse()
+def kernel_table(stats, total_ms, peak):
+    kernels = {}
+    for s in stats:
+        avg_us = 1e3 * s["ms"] / max(s["launches"], 1)
+        ent = {"launches": s["launches"], "avg_us": round(avg_us, 2)}
+        if total_ms:
+            ent["share"] = round(s["ms"] / max(total_ms, 1e-9), 4)
+        if s["flops"] > 0:
+            tf = s["flops"] / (s["ms"] * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), frac=round(tf / peak, 4))
+        else:
+            gbs = s["bytes"] / (s["ms"] * 1e-3) / 1e9
+            ent.update(gbs=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[s["name"]] = ent
+    return kernels
+
+
+class Workload:
+    """One workload resident on the GPU, with its step arguments and workspace."""
+
+    def __init__(self, wl, kind, torch, np, mns, synthetic, dev):
+        self.wl, self.kind, self.torch, self.mns = wl, kind, torch, mns
+        restarts = wl.restart_before if kind == "gram" else ()
+        if kind == "gram" and not restarts:
+            restarts = (3,)
+        self.W, self.M, self.G, self.V = build_inputs(wl, torch, np, synthetic, dev)
+        self.kw = dict(mu=wl.mu, lr=wl.lr, coeffs=wl.coeff_table(), kind=kind,
+                       restart_before=restarts, normuon=wl.normuon, beta2=wl.beta2, eps=wl.eps,
+                       row_fraction=wl.row_fraction)
+        self.v_arg = self.V if wl.normuon else None
+        self.ws = torch.empty(mns.step_workspace_size(self.W, self.M, self.G, self.v_arg, **self.kw),
+                              dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self):
+        self.mns.muon_step(self.W, self.M, self.G, self.v_arg, workspace=self.ws,
+                           stream=self.stream, **self.kw)
+
+    def run(self, steps, profile=False, flush=None):
+        """`steps` steps between two synchronisations; returns (ms per step, kernel stats or
+        None). With `profile` the library records a hipEvent pair around each launch; with
+        `flush` (a device buffer) it writes over it before each HBM-bound launch."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if profile:
+            self.mns.profile_begin()
+            if flush is not None:
+                self.mns.profile_set_flush(flush)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(steps):
+            self.step()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        stats = self.mns.profile_end() if profile else None
+        return e0.elapsed_time(e1) / steps, stats
+
+    def free(self):
+        del self.W, self.M, self.G, self.V, self.ws
+
+
+def gemm_phase(stats, steps):
+    gemm = [s for s in stats if s["flops"] > 0]
+    flops = sum(s["flops"] for s in gemm) / steps
+    ms = sum(s["ms"] for s in gemm) / steps
+    return flops, ms
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.calibrate_copy:
         calibrate_copy()
         return
@@ -207,77 +350,97 @@ def main():
     import muon_newton_schulz_amd as mns
     import synthetic
 
-    wl = synthetic.WORKLOADS[args.config]
-    kind = args.kind or wl.kind
-    restarts = wl.restart_before if kind == "gram" else ()
-    if kind == "gram" and not restarts:
-        restarts = (3,)
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     dev = torch.device("cuda:0")
-    W, M, G, V = build_inputs(wl, torch, np, synthetic, dev)
-    kw = dict(mu=wl.mu, lr=wl.lr, coeffs=wl.coeff_table(), kind=kind, restart_before=restarts,
-              normuon=wl.normuon, beta2=wl.beta2, eps=wl.eps, row_fraction=wl.row_fraction)
-    v_arg = V if wl.normuon else None
-    ws = torch.empty(mns.step_workspace_size(W, M, G, v_arg, **kw), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        mns.muon_step(W, M, G, v_arg, workspace=ws, stream=stream, **kw)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    mns.profile_begin()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    stats = mns.profile_end()
-    total_ms = e0.elapsed_time(e1)
-    ms_step = total_ms / args.steps
-
-    gemm = [s for s in stats if s["flops"] > 0]
-    ns_flops = sum(s["flops"] for s in gemm) / args.steps
-    ns_ms = sum(s["ms"] for s in gemm) / args.steps
+    wl = synthetic.WORKLOADS[args.workload]
+    kind = args.kind or wl.kind
     dtype = "f32" if wl.storage == "f32" else "f16"
     peak = PEAK_TFLOPS[dtype]
-    value = ns_flops / (ms_step * 1e-3) / 1e12
 
-    kernels = {}
-    for s in stats:
-        avg_us = 1e3 * s["ms"] / max(s["launches"], 1)
-        ent = {"launches": s["launches"], "avg_us": round(avg_us, 2),
-               "share": round(s["ms"] / max(total_ms, 1e-9), 4)}
-        if s["flops"] > 0:
-            tf = s["flops"] / (s["ms"] * 1e-3) / 1e12
-            ent.update(tflops=round(tf, 1), frac=round(tf / peak, 4))
-        else:
-            gbs = s["bytes"] / (s["ms"] * 1e-3) / 1e9
-            ent.update(gbs=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4))
-        kernels[s["name"]] = ent
+    say(f"workload {args.workload}: {wl.name}; building inputs")
+    t0 = time.perf_counter()
+    work = Workload(wl, kind, torch, np, mns, synthetic, dev)
+    say(f"inputs resident ({time.perf_counter() - t0:.1f} s); warm-up")
+    work.run(args.warmup)
+
+    # The timed steps, with the per-launch events (the roofline's source).
+    say(f"timing {args.steps} steps")
+    ms_step, stats = work.run(args.steps, profile=True)
+    total_ms = ms_step * args.steps
+    ns_flops, ns_ms = gemm_phase(stats, args.steps)
+    value = ns_flops / (ms_step * 1e-3) / 1e12
+    dense_eq = dense_equivalent_flops(wl) if kind == "standard" else None
+    kernels = kernel_table(stats, total_ms, peak)
 
     dom = max(stats, key=lambda s: s["ms"])
+    traffic_key = f"workload{args.workload}-{kind}"
     if dom["flops"] > 0:
         ach = dom["flops"] / dom["launches"] / (dom["ms"] / dom["launches"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom["name"], "achieved": round(ach, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                "traffic": measured_traffic(dom["name"], f"config{args.config}-{kind}")}
+                "traffic": measured_traffic(dom["name"], traffic_key),
+                "flops_per_launch": dom["flops"] / dom["launches"],
+                "avg_launch_us": round(1e3 * dom["ms"] / dom["launches"], 2)}
     else:
         ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom["name"], "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic(dom["name"], f"config{args.config}-{kind}")}
+                "traffic": measured_traffic(dom["name"], traffic_key),
+                "bytes_per_launch": dom["bytes"] / dom["launches"],
+                "avg_launch_us": round(1e3 * dom["ms"] / dom["launches"], 2)}
+
+    # The same steps without the per-launch events (their overhead, for reference).
+    say("uninstrumented steps")
+    ms_plain, _ = work.run(args.steps)
+
+    # The HBM kernels with the Infinity Cache flushed before each launch.
+    flushed = None
+    if not args.no_flush_pass:
+        say("cache-flushed HBM kernel timing")
+        buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        n_fl = max(1, min(args.steps, 5))
+        _, fstats = work.run(n_fl, profile=True, flush=buf)
+        del buf
+        big = [s for s in fstats if s["flops"] == 0 and s["bytes"] / s["launches"] >= 16 << 20]
+        flushed = kernel_table(big, 0, peak)   # the launches that moved >= 16 MiB (flushed ones)
+        flushed = {"steps": n_fl, "flush_bytes": FLUSH_BYTES, "gate": HBM_GATE, "kernels": flushed}
 
     graph = None
     if not args.no_graph:
-        graph = graph_timing(mns, torch, step_args=(W, M, G, v_arg), ws=ws, kw=kw,
-                             warmup=args.warmup, steps=args.steps)
+        say("graph replay")
+        graph = graph_timing(mns, torch, step_args=(work.W, work.M, work.G, work.v_arg),
+                             ws=work.ws, kw=work.kw, warmup=args.warmup, steps=args.steps)
         graph["eager_ms_per_step"] = round(ms_step, 4)
+    work.free()
+    del work
+    torch.cuda.empty_cache()
+
+    gate = None
+    if not args.no_gate and args.workload != GATE_WORKLOAD:
+        gwl = synthetic.WORKLOADS[GATE_WORKLOAD]
+        say(f"gate workload: {gwl.name}, standard NS")
+        gw = Workload(gwl, "standard", torch, np, mns, synthetic, dev)
+        gw.run(args.warmup)
+        g_ms, g_stats = gw.run(args.steps, profile=True)
+        g_flops, g_ns_ms = gemm_phase(g_stats, args.steps)
+        g_plain, _ = gw.run(args.steps)
+        gate_tf = g_flops / (g_ns_ms * 1e-3) / 1e12
+        gate = {"workload": gwl.name, "ns": "standard", "ms_per_step": round(g_ms, 4),
+                "ms_per_step_uninstrumented": round(g_plain, 4),
+                "ns_gemm_ms_per_step": round(g_ns_ms, 4), "ns_gemm_tflops": round(gate_tf, 1),
+                "ns_gemm_frac": round(gate_tf / PEAK_TFLOPS["f16"], 4), "gate": MFMA_GATE,
+                "step_tflops": round(g_flops / (g_ms * 1e-3) / 1e12, 1),
+                "dense_equivalent_tflops": round(dense_equivalent_flops(gwl) / (g_ms * 1e-3) / 1e12, 1),
+                "kernels": kernel_table(g_stats, g_ms * args.steps, PEAK_TFLOPS["f16"])}
+        gw.free()
+        del gw
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
+        say("oracle sample on the host")
         cpu = cpu_baseline(wl, kind, args.cpu_seconds)
 
     out = {
@@ -291,17 +454,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if wl.storage == "bf16" else "f32",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "ns": kind, "T": wl.T, "normuon": wl.normuon,
                    "row_fraction": wl.row_fraction, "matrices": wl.n_matrices,
                    "storage": wl.storage},
+        "ms_per_step_uninstrumented": round(ms_plain, 4),
         "ns_gemm_ms_per_step": round(ns_ms, 4),
         "ns_gemm_tflops": round(ns_flops / (ns_ms * 1e-3) / 1e12, 1) if ns_ms > 0 else None,
         "ns_flops_per_step": ns_flops,
+        "dense_equivalent_flops_per_step": dense_eq,
+        "dense_equivalent_tflops": round(dense_eq / (ms_step * 1e-3) / 1e12, 1) if dense_eq else None,
         "mfma_frac_step": round(value / peak, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "ns_gate_4096x16384": gate,
+        "hbm_kernels_cache_flushed": flushed,
         "graph": graph,
         "kernels": kernels,
     }

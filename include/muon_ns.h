@@ -87,7 +87,7 @@ typedef struct mns_matrix {
  *   T, abc        T >= 1 Newton-Schulz iterations; abc (host) holds 3*T floats
  *                 a_1, b_1, c_1, a_2, ... of the odd quintics p_t(x) = a x + b x^3 + c x^5
  *   kind          mns_ns_kind
- *   restart_mask  Gram NS only: bit t set (2 <= t <= T) = restart before iteration t
+ *   restart_mask  Gram NS only: bit t set (2 <= t <= min(T, 31)) = restart before iteration t
  *                 (X <- Q X, Gram matrix recomputed, Q <- I). Must be 0 for standard NS.
  *   normuon       0 = Muon update W -= lr * O; 1 = NorMuon (Eq. 2) with beta2, eps
  *   row_fraction  Dion3 f in (0, 1]: 1 = every row (plain Muon/NorMuon); f < 1 selects the
@@ -185,6 +185,16 @@ typedef struct mns_kernel_stat {
 
 mns_status mns_profile_begin(void);
 mns_status mns_profile_end(mns_kernel_stat* out, int capacity, int* count);
+
+/* Cache flush for the session's HBM timings: while the session is open, every launch that
+ * reports no FLOPs and at least 16 MiB of algorithmic bytes (the elementwise and reduction
+ * kernels) is preceded, outside its event pair, by a kernel that writes `bytes` bytes of
+ * zeros over `buffer` (device memory the caller owns, 16-byte aligned; 1 GiB or more evicts
+ * the 256 MB Infinity Cache), so that the timed launch reads its operands from HBM rather
+ * than from a cache an earlier kernel filled. buffer = NULL or bytes = 0 turns it off;
+ * mns_profile_end turns it off. MNS_ERR_PARAM when no session is open or `buffer` is
+ * misaligned. The flush launches are not recorded. */
+mns_status mns_profile_set_flush(void* buffer, size_t bytes);
 
 #ifdef __cplusplus
 }

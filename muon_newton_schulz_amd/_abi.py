@@ -25,6 +25,7 @@ EXPORTS = (
     "mns_status_string", "mns_version", "mns_step_workspace_size", "muon_step",
     "mns_ns_workspace_size", "ns_orthogonalize", "gram_ns_orthogonalize",
     "mns_normuon_workspace_size", "normuon_scale", "mns_profile_begin", "mns_profile_end",
+    "mns_profile_set_flush",
 )
 
 
@@ -116,6 +117,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mns_profile_end.restype = ctypes.c_int
     lib.mns_profile_end.argtypes = [ctypes.POINTER(MnsKernelStat), ctypes.c_int,
                                     ctypes.POINTER(ctypes.c_int)]
+    lib.mns_profile_set_flush.restype = ctypes.c_int
+    lib.mns_profile_set_flush.argtypes = [vp, ctypes.c_size_t]
     _lib = lib
     return lib
 

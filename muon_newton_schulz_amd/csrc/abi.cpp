@@ -8,6 +8,7 @@
 #include "muon_ns.h"
 #include "mns_internal.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -25,16 +26,37 @@ struct ProfRec {
   hipEvent_t a, b;
   double flops, bytes;
 };
+// g_prof_on is read on every launch without the lock (atomic: a session toggled on another
+// thread is seen cleanly); the record list and the failure flag are guarded by g_prof_mu.
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
 bool g_prof_failed = false;
 std::vector<ProfRec> g_prof;
+// Optional cache flush before the session's HBM-bound launches (mns_profile_set_flush).
+void* g_flush_buf = nullptr;
+size_t g_flush_bytes = 0;
+constexpr double kFlushMinBytes = double(16 << 20);
 
 template <typename F>
 hipError_t timed(const char* name, double flops, double bytes, hipStream_t s, F&& launch) {
-  if (!g_prof_on) return launch();
+  if (!g_prof_on.load(std::memory_order_acquire)) return launch();
+  {
+    void* fb = nullptr;
+    size_t fn = 0;
+    {
+      std::lock_guard<std::mutex> lk(g_prof_mu);
+      fb = g_flush_buf;
+      fn = g_flush_bytes;
+    }
+    // outside the event pair: the launch then reads its operands from HBM
+    if (fb && fn && flops == 0.0 && bytes >= kFlushMinBytes) {
+      const hipError_t fe = cache_flush(fb, fn, s);
+      if (fe != hipSuccess) return fe;
+    }
+  }
   ProfRec r{name, nullptr, nullptr, flops, bytes};
   if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof_failed = true;
     return launch();
   }
@@ -267,6 +289,12 @@ mns_status run_standard(const Geo& g, int count, const NsBuffers& b, int T, cons
 // Gram Newton-Schulz (Theorem 2) with restarts (Algorithm 3): R = X X^T; per iteration
 // Z = a I + b R + c R^2, R <- R Z^2 (skipped when unused), Q <- Q Z (Q_1 = Z_1);
 // a restart before t forms X <- Q X, R <- X X^T, Q <- I. Output Q X (stored layout).
+// Whether restart_mask asks for a restart before iteration t (bits 2..31; a 32-bit mask
+// cannot name a later iteration, and a shift by 32 or more would be undefined).
+inline bool restart_at(uint32_t restart_mask, int t) {
+  return t >= 0 && t < 32 && ((restart_mask >> t) & 1u);
+}
+
 mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const float* abc,
                     uint32_t restart_mask, hipStream_t s, void** out, RowSq* rs) {
   int cur = 0;
@@ -287,7 +315,7 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
   bool q_identity = true;
   for (int t = 1; t <= T; ++t) {
     const float a = abc[3 * (t - 1)], bb = abc[3 * (t - 1) + 1], c = abc[3 * (t - 1) + 2];
-    if (t > 1 && ((restart_mask >> t) & 1u)) {
+    if (t > 1 && restart_at(restart_mask, t)) {
       if (!q_identity) {
         MNS_HIP(timed_gemm(lx_desc(g, count, b, km, Q, cur, b.X[cur ^ 1],
                                    km ? nullptr : b.Xt[cur ^ 1]),
@@ -306,7 +334,7 @@ mns_status run_gram(const Geo& g, int count, const NsBuffers& b, int T, const fl
     zd.gamma = a;
     zd.diag_limit = (int)g.n;
     MNS_HIP(timed_gemm(zd, nn * g.n, s));
-    if (t < T && !((restart_mask >> (t + 1)) & 1u)) {
+    if (t < T && !restart_at(restart_mask, t + 1)) {
       MNS_HIP(timed_gemm(sym_desc(g, count, b, Z, Z, g.ld_q, b.sq_stride, n, Z2), nn * g.n, s));
       MNS_HIP(timed_gemm(sym_desc(g, count, b, R, Z2, g.ld_q, b.sq_stride, n, Rt), nn * g.n, s));
       void* tmp = R; R = Rt; Rt = tmp;
@@ -745,14 +773,25 @@ mns_status mns_profile_begin(void) {
   }
   g_prof.clear();
   g_prof_failed = false;
-  g_prof_on = true;
+  g_prof_on.store(true, std::memory_order_release);
+  return MNS_OK;
+}
+
+mns_status mns_profile_set_flush(void* buffer, size_t bytes) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on.load()) return MNS_ERR_PARAM;
+  if (buffer && !aligned(buffer, 16)) return MNS_ERR_PARAM;
+  g_flush_buf = bytes ? buffer : nullptr;
+  g_flush_bytes = buffer ? bytes : 0;
   return MNS_OK;
 }
 
 mns_status mns_profile_end(mns_kernel_stat* out, int capacity, int* count) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on) return MNS_ERR_PARAM;
-  g_prof_on = false;
+  if (!g_prof_on.load()) return MNS_ERR_PARAM;
+  g_prof_on.store(false, std::memory_order_release);
+  g_flush_buf = nullptr;
+  g_flush_bytes = 0;
   std::vector<mns_kernel_stat> stats;
   bool ok = !g_prof_failed;
   for (ProfRec& r : g_prof) {

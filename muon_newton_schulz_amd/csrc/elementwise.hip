@@ -435,6 +435,14 @@ __global__ __launch_bounds__(kThreads) void k_normuon_ratio(const double* fin, i
   for (int64_t i = threadIdx.x; i < rows; i += kThreads) rs[i] = rs[i] * scale;
 }
 
+// Cache flush for timings: zeros written over a large scratch buffer with 16-byte stores.
+__global__ __launch_bounds__(kThreads) void k_flush(uint4* p, int64_t n16) {
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads)
+    p[i] = z;
+}
+
 __global__ __launch_bounds__(kThreads) void k_fill(float* p, int64_t n, float value) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kThreads)
@@ -799,6 +807,13 @@ hipError_t fill(float* p, int64_t n, float value, hipStream_t s) {
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_fill, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, n, value);
+  return last();
+}
+
+hipError_t cache_flush(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 < 1) return hipSuccess;
+  hipLaunchKernelGGL(k_flush, dim3(8192), dim3(kThreads), 0, s, static_cast<uint4*>(p), n16);
   return last();
 }
 

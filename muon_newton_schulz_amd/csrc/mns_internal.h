@@ -135,6 +135,10 @@ hipError_t normuon_finalize(const float* part, int chunks, int count, int64_t ro
                             float inv_s2, float out_scale, float* rowscale, double* fin,
                             hipStream_t s);
 
+// Writes zeros over `bytes` (rounded down to 16) of device memory p (16-byte aligned): the
+// cache flush of the profiling session's HBM timings.
+hipError_t cache_flush(void* p, size_t bytes, hipStream_t s);
+
 // rowscale[b][i] = value (plain Muon: every row scaled alike).
 hipError_t fill(float* p, int64_t n, float value, hipStream_t s);
 

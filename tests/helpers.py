@@ -56,3 +56,24 @@ def check_weight(W_gpu, W0, delta_ref, storage: str, what: str = "W") -> float:
     bound = TOL[storage] * np.linalg.norm(delta_ref) + np.linalg.norm(ulp_half(W0 + delta_ref, storage))
     assert err <= bound, f"{what}: |W - W0 - delta| = {err:.4g} > bound {bound:.4g}"
     return float(err / max(np.linalg.norm(delta_ref), 1e-300))
+
+
+def dion3_rows_used(M0, G, M1, W0, W1, k: int, what: str = "") -> np.ndarray:
+    """The rows a Dion3 step on the GPU selected, for re-running the oracle on them.
+
+    A selected row is decayed (M1 differs from float32(M0 + G), the one rounding an
+    unselected row gets) or updated (W1 differs from W0). The GPU ranks float32 l1 norms,
+    the oracle float64 ones: a row may differ from the oracle's choice only where its
+    float64 norm lies within 1e-5 relative of the k-th largest."""
+    Mg = np.asarray(M0, dtype=np.float64) + np.asarray(G, dtype=np.float64)
+    Mg32 = Mg.astype(np.float32).astype(np.float64)
+    sel_gpu = np.where(np.any(np.asarray(M1) != Mg32, axis=1) |
+                       np.any(np.asarray(W1) != np.asarray(W0), axis=1))[0]
+    S_orc = oracle.select_rows(Mg, k)
+    l1 = np.abs(Mg).sum(axis=1)
+    kth = np.sort(l1)[::-1][k - 1]
+    diff = np.setxor1d(sel_gpu, S_orc)
+    assert all(abs(l1[i] - kth) <= 1e-5 * kth for i in diff), (what, diff[:10])
+    rows = sel_gpu if len(diff) else S_orc
+    assert len(rows) == k, (what, len(rows), k)
+    return np.sort(rows)

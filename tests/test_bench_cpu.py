@@ -45,3 +45,33 @@ def test_build_inputs_bf16_bits_preserved():
 
 def test_traffic_lookup_unknown_kernel_is_none():
     assert bench.measured_traffic("no_such_kernel", "config2-standard") is None
+
+
+def test_dense_equivalent_counts():
+    # T (4 m n^2 + 2 n^3) per matrix, summed: 4 x 4096^2 -> 8.25e12, 4096x16384 -> 6.18e12,
+    # the 196-matrix layer set -> 2.516e14 (tall matrices counted on their short side)
+    assert abs(bench.dense_equivalent_flops(synthetic.WORKLOADS[2]) / 8.246e12 - 1) < 1e-3
+    assert abs(bench.dense_equivalent_flops(synthetic.WORKLOADS[3]) / 6.185e12 - 1) < 1e-3
+    assert abs(bench.dense_equivalent_flops(synthetic.WORKLOADS[4]) / 2.516e14 - 1) < 1e-3
+    # Dion3 orthogonalises k = ceil(f rows) rows
+    assert bench.ns_shapes(synthetic.WORKLOADS[5]) == [(1280, 13824)]
+
+
+def test_default_workload_is_the_layer_set():
+    args = bench.parse([])
+    assert args.workload == 4 and synthetic.WORKLOADS[4].n_matrices == 196
+    assert bench.parse(["--config", "2"]).workload == 2
+
+
+def test_parallel_gradients_equal_serial():
+    wl = dataclasses.replace(synthetic.WORKLOADS[4], groups=(synthetic.configs.MatrixSpec(64, 96, 3),
+                                                             synthetic.configs.MatrixSpec(96, 64, 2)))
+    got = list(bench.gradient_bits(wl, synthetic, threads=4))
+    for (idx, r, c), g in zip(wl.matrices(), got):
+        assert np.array_equal(g, synthetic.gradient(wl.dist, r, c, wl.storage, wl.index, 0, idx))
+
+
+def test_host_info_fields():
+    info, threads = bench.host_info()
+    assert info["os_cpu_count"] == os.cpu_count()
+    assert "cpu_model" in info and "blas" in info

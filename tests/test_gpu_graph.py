@@ -1,14 +1,16 @@
 """The Muon step under HIP graph capture (the grouped step recorded once and replayed, to
 remove per-launch overhead on small matrices): every replay, with the program's own eager
 work and synchronisations between replays, must equal the same step run eagerly, bit for
-bit (every kernel of the step is deterministic)."""
+bit (every kernel of the step is deterministic), and must match the fp64 oracle's step
+from the same pre-step state (W, M, v) to the parity gate."""
 import numpy as np
 import pytest
 import torch
 
 import muon_newton_schulz_amd as mns
+import oracle
 import synthetic
-from helpers import to_device
+from helpers import TOL, check_weight, dion3_rows_used, rel, stored_f64, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -62,9 +64,14 @@ def test_step_graph_replays_match_eager(case):
     with torch.cuda.graph(graph):
         mns.muon_step(Wg, Mg, G, Vg, workspace=ws_g, stream=torch.cuda.current_stream(), **common)
     torch.cuda.synchronize()
+    okw = dict(mu=common["mu"], lr=common["lr"], coeffs=common["coeffs"], kind=common["kind"],
+               restart_before=common.get("restart_before", ()), normuon=common["normuon"],
+               beta2=common["beta2"], eps=common["eps"], storage=storage)
+    f = common["row_fraction"]
     for step in range(4):
         fill_gradients(step)                      # eager work between replays
         torch.cuda.synchronize()
+        pre = [(to_f64(Wg[i]), to_f64(Mg[i]), to_f64(Vg[i])) for i in range(len(shapes))]
         graph.replay()
         torch.cuda.synchronize()
         mns.muon_step(We, Me, G, Ve, workspace=ws_e, **common)
@@ -74,4 +81,23 @@ def test_step_graph_replays_match_eager(case):
             assert torch.equal(Mg[i], Me[i]), (step, i, "M")
             assert torch.equal(Vg[i], Ve[i]), (step, i, "v")
         assert any(not torch.equal(Wg[i], W0[i]) for i in range(len(shapes)))
-        _say(f"  replay {step}: identical to the eager step")
+        # the replayed step against the oracle's step from the same pre-step state
+        errs = []
+        for i, (r, c) in enumerate(shapes):
+            W_pre, M_pre, V_pre = pre[i]
+            g64 = stored_f64(synthetic.gradient("student_t", r, c, storage, 963, step, i), storage)
+            W1, M1, V1 = to_f64(Wg[i]), to_f64(Mg[i]), to_f64(Vg[i])
+            v_in = V_pre if common["normuon"] else None
+            if f < 1.0:
+                k = oracle.rows_for_fraction(f, r)
+                rows = dion3_rows_used(M_pre, g64, M1, W_pre, W1, k, f"replay {step} matrix {i}")
+                ref = oracle.dion3_step(W_pre, M_pre, g64, f=f, rows=rows, v=v_in, **okw)
+            else:
+                ref = oracle.muon_step(W_pre, M_pre, g64, v=v_in, **okw)
+            assert rel(M1, ref["M"]) < 1e-6, (step, i, "M")
+            if common["normuon"]:
+                assert rel(V1, ref["v"]) < TOL[storage], (step, i, "v")
+            errs.append(check_weight(W1, W_pre, ref["W_exact"] - W_pre, storage,
+                                     f"replay {step} W[{i}]"))
+        _say(f"  replay {step}: identical to the eager step; vs oracle worst update rel err "
+             f"{max(errs):.2e}")

@@ -3,8 +3,9 @@ uses (one muon_step call over all of a workload's matrices), against the fp64 or
 
 Gate: relative Frobenius error <= 1e-4 (float32 storage) / 2e-2 (bfloat16), per matrix and
 after each step; multi-step workloads are re-synced, i.e. the oracle starts every step from
-the GPU's state. The 196-matrix layer set checks the first layer's 7 matrices against the
-oracle and all 196 against invariants that hold at any size.
+the GPU's state. The 196-matrix layer set checks the first layer's 7 matrices and one matrix
+of every launch chunk against the oracle, and all 196 against invariants that hold at any
+size.
 """
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ import torch
 import oracle
 import muon_newton_schulz_amd as mns
 import synthetic
-from helpers import TOL, check_weight, rel, stored_f64, to_device, to_f64
+from helpers import TOL, check_weight, dion3_rows_used, rel, stored_f64, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -112,7 +113,10 @@ def test_config4_layer_set_grouped():
     _say("config 4:", wl.name)
     mats = wl.matrices()
     W, M, G, V, Gs = [], [], [], [], {}
-    first_layer = {0, 1, 2, 3, 112, 113, 168}
+    # the first layer's seven matrices, and one matrix from every 32-matrix launch chunk of
+    # each shape group (square: 0-31, 32-63, 64-95, 96-111; wide: 112-143, 144-167; tall:
+    # 168-195), so a packing or workspace error in any chunk shows against the oracle
+    first_layer = {0, 1, 2, 3, 112, 113, 168, 40, 70, 100, 111, 150, 167, 195}
     for idx, r, c in mats:
         g = synthetic.gradient(wl.dist, r, c, "bf16", 4, 0, idx)
         if idx in first_layer:
@@ -136,7 +140,7 @@ def test_config4_layer_set_grouped():
         assert abs(dw / (wl.lr * o_norm) - 1.0) < 5e-3, (idx, float(dw / (wl.lr * o_norm)))
         rn = torch.linalg.norm(wf, dim=1)
         assert float(rn.max() / rn.min()) < 1.02, (idx, float(rn.max() / rn.min()))
-    # full oracle on the first layer's seven matrices
+    # full oracle on the first layer and on one matrix of every launch chunk
     for idx in sorted(first_layer):
         _, r, c = mats[idx]
         _say(f"  matrix {idx} ({r}x{c}): oracle")
@@ -162,21 +166,11 @@ def test_config5_dion3_ten_steps_resynced():
         mns.muon_step(W, M, to_device(g, "bf16"), V, **_kw(wl))
         torch.cuda.synchronize()
         g64 = stored_f64(g, "bf16")
-        # selection: the rows whose momentum the GPU decayed
         M1, W1 = to_f64(M), to_f64(W)
-        Mg = M0 + g64
-        # an unselected row keeps M0 + G, rounded once to float32 (one IEEE addition)
-        Mg32 = Mg.astype(np.float32).astype(np.float64)
-        sel_gpu = np.where(np.any(M1 != Mg32, axis=1) | np.any(W1 != W0, axis=1))[0]
-        S_orc = oracle.select_rows(Mg, k)
-        l1 = np.abs(Mg).sum(axis=1)
-        kth = np.sort(l1)[::-1][k - 1]
-        diff = np.setxor1d(sel_gpu, S_orc)
-        # rows may swap only at float32-vs-float64 near-ties of the l1 norm
-        assert all(abs(l1[i] - kth) <= 1e-5 * kth for i in diff), (step, diff[:10])
-        rows_used = sel_gpu if len(diff) else S_orc
-        assert len(rows_used) == k
-        ref = oracle.dion3_step(W0, M0, g64, rows=np.sort(rows_used), storage="bf16", v=V0,
+        # the rows the GPU selected (swaps allowed only at float32-vs-float64 near-ties)
+        rows_used = dion3_rows_used(M0, g64, M1, W0, W1, k, f"step {step}")
+        diff = np.setxor1d(rows_used, oracle.select_rows(M0 + g64, k))
+        ref = oracle.dion3_step(W0, M0, g64, rows=rows_used, storage="bf16", v=V0,
                                 f=wl.row_fraction, **_oracle_kw(wl))
         assert rel(M1, ref["M"]) < 1e-6, step
         assert rel(to_f64(V), ref["v"]) < TOL["bf16"], step
