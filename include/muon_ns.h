@@ -150,6 +150,25 @@ mns_status gram_ns_orthogonalize(const void* X, void* O, int dtype, int64_t batc
                                  const float* abc /* (host) 3*T */, uint32_t restart_mask,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free variant of ns_orthogonalize, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. The same standard quintic Newton-Schulz as ns_orthogonalize, with
+ * every scratch buffer carved from a 64 MiB array of device memory inside the library (one
+ * per GPU, held until the process ends); the caller passes only X and O. Nothing is
+ * allocated, and no library routine that allocates is called.
+ *   Sizes: a batch runs in chunks of up to 32 matrices that fit the array; a problem whose
+ *   single-matrix buffers exceed 64 MiB (about 2 x 2 iterates of rows x cols plus two
+ *   short-side squares, each dimension rounded up to 256 and widened by 256; for bfloat16 up
+ *   to e.g. 2048 x 2048 or 1024 x 4096) returns MNS_ERR_WORKSPACE before anything is enqueued.
+ *   Other arguments and errors as ns_orthogonalize; the result equals its result up to the
+ *   order of split-k partial sums (bit-identical when the chunking and split-k scratch agree).
+ *   Concurrency: every call on one GPU uses that GPU's single array, which keeps the last
+ *   call's contents (each call writes every word before reading it). Calls that may overlap
+ *   on one GPU -- on different streams, or from different threads -- race; serialise them. */
+mns_status ns_orthogonalize_noalloc(const void* X, void* O, int dtype, int64_t batch,
+                                    int64_t rows, int64_t cols, int T,
+                                    const float* abc /* (host) 3*T */, void* stream);
+
 /* Workspace bytes for normuon_scale. */
 mns_status mns_normuon_workspace_size(int64_t batch, int64_t rows, int64_t cols,
                                       size_t* bytes /* (host) out */);

@@ -16,7 +16,8 @@ from . import _abi
 from ._abi import (MNS_BF16, MNS_F32, MNS_NS_GRAM, MNS_NS_STANDARD, MnsError,  # noqa: F401
                    MnsHparams, MnsMatrix, check, load)
 
-__all__ = ["muon_step", "ns_orthogonalize", "gram_ns_orthogonalize", "normuon_scale",
+__all__ = ["muon_step", "ns_orthogonalize", "ns_orthogonalize_noalloc",
+           "gram_ns_orthogonalize", "normuon_scale",
            "step_workspace_size", "ns_workspace_size", "normuon_workspace_size",
            "restart_mask", "profile_begin", "profile_set_flush", "profile_end", "MnsError",
            "load"]
@@ -251,6 +252,19 @@ def ns_orthogonalize(X: torch.Tensor, coeffs, out: torch.Tensor | None = None,
     check(lib.ns_orthogonalize(_ptr(X), _ptr(O), _dtype_code(X), b, r, c, T, abc,
                                ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)),
           "ns_orthogonalize")
+    return O
+
+
+def ns_orthogonalize_noalloc(X: torch.Tensor, coeffs, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """ns_orthogonalize without a workspace: the library's own device scratch (64 MiB per GPU)
+    holds every buffer, so the call allocates nothing (graph capture, serving loops). `out`
+    must be given; overlapping calls on one GPU race."""
+    if out is None:
+        raise ValueError("ns_orthogonalize_noalloc: out must be given (nothing is allocated)")
+    b, r, c, O = _ns_operands(X, out, "ns_orthogonalize_noalloc")
+    abc, T = _coeffs(coeffs)
+    check(load().ns_orthogonalize_noalloc(_ptr(X), _ptr(O), _dtype_code(X), b, r, c, T, abc,
+                                          _stream(stream)), "ns_orthogonalize_noalloc")
     return O
 
 

@@ -25,7 +25,7 @@ EXPORTS = (
     "mns_status_string", "mns_version", "mns_step_workspace_size", "muon_step",
     "mns_ns_workspace_size", "ns_orthogonalize", "gram_ns_orthogonalize",
     "mns_normuon_workspace_size", "normuon_scale", "mns_profile_begin", "mns_profile_end",
-    "mns_profile_set_flush",
+    "mns_profile_set_flush", "ns_orthogonalize_noalloc",
 )
 
 
@@ -117,6 +117,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mns_profile_end.restype = ctypes.c_int
     lib.mns_profile_end.argtypes = [ctypes.POINTER(MnsKernelStat), ctypes.c_int,
                                     ctypes.POINTER(ctypes.c_int)]
+    lib.ns_orthogonalize_noalloc.restype = ctypes.c_int
+    lib.ns_orthogonalize_noalloc.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int,
+                                             fp, vp]
     lib.mns_profile_set_flush.restype = ctypes.c_int
     lib.mns_profile_set_flush.argtypes = [vp, ctypes.c_size_t]
     _lib = lib

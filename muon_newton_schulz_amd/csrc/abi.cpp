@@ -145,7 +145,15 @@ struct NsBuffers {
   int64_t x_stride = 0, xt_stride = 0, sq_stride = 0;   // batch strides (elements)
 };
 
-void carve_ns(Carver& cv, const Geo& g, int count, int kind, NsBuffers& b) {
+// Split-k scratch the GEMMs of this geometry can use at most: (output tiles) x (k-tiles / 8)
+// float32 tiles (before any cap).
+size_t gemm_scratch_need(const Geo& g, int count) {
+  const size_t kparts = (size_t)(g.m_p > g.n_p ? g.m_p : g.n_p) / 256;
+  return (size_t)count * g.n_p * g.n_p * kparts * sizeof(float);
+}
+
+void carve_ns(Carver& cv, const Geo& g, int count, int kind, NsBuffers& b,
+              size_t gemm_cap = kGemmScratchBytes) {
   const size_t es = (size_t)elem_bytes(g.elem);
   b.x_stride = g.n_p * g.ld_x;
   b.xt_stride = g.m_p * g.ld_t;
@@ -156,10 +164,10 @@ void carve_ns(Carver& cv, const Geo& g, int count, int kind, NsBuffers& b) {
   }
   const int nsq = kind == MNS_NS_GRAM ? 6 : 2;
   for (int i = 0; i < nsq; ++i) b.sq[i] = cv.take<char>(es * count * b.sq_stride);
-  // split-k partial sums: at most (output tiles) x (k-tiles / 8) tiles of float32, capped
-  const size_t kparts = (size_t)(g.m_p > g.n_p ? g.m_p : g.n_p) / 256;
-  size_t scratch = (size_t)count * g.n_p * g.n_p * kparts * sizeof(float);
-  if (scratch > kGemmScratchBytes) scratch = kGemmScratchBytes;
+  // split-k partial sums: at most (output tiles) x (k-tiles / 8) tiles of float32, capped (a
+  // smaller cap only makes the GEMMs split their tail tiles into fewer parts)
+  size_t scratch = gemm_scratch_need(g, count);
+  if (scratch > gemm_cap) scratch = gemm_cap;
   b.gemm_scratch = cv.take<float>(scratch / sizeof(float));
   b.gemm_scratch_bytes = scratch;
 }
@@ -624,13 +632,14 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
 // ---- standalone orthogonalisation ------------------------------------------------------------
 
 static size_t ns_bytes(const Geo& g, int c, int kind, int64_t rows, int64_t cols,
-                       NsBuffers* b, float** partials, float** xscale, void* base) {
+                       NsBuffers* b, float** partials, float** xscale, void* base,
+                       size_t gemm_cap = kGemmScratchBytes) {
   Carver cv(base);
   NsBuffers tmp;
   NsBuffers& nb = b ? *b : tmp;
   float* p = cv.take<float>((size_t)c * norm_blocks(rows * cols));
   float* x = cv.take<float>((size_t)c);
-  carve_ns(cv, g, c, kind, nb);
+  carve_ns(cv, g, c, kind, nb, gemm_cap);
   if (partials) *partials = p;
   if (xscale) *xscale = x;
   return cv.off + 256;
@@ -652,9 +661,10 @@ mns_status mns_ns_workspace_size(int dtype, int64_t batch, int64_t rows, int64_t
   return MNS_OK;
 }
 
-static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch, int64_t rows,
-                                int64_t cols, int T, const float* abc, int kind,
-                                uint32_t restart_mask, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks shared by the orthogonalisation entry points (everything but the workspace).
+static mns_status check_orthogonalize(const void* X, void* O, int dtype, int64_t batch,
+                                      int64_t rows, int64_t cols, int T, const float* abc,
+                                      int kind, uint32_t restart_mask) {
   mns_status st = check_dtype(dtype);
   if (st != MNS_OK) return st;
   st = check_shape(batch, rows, cols);
@@ -665,18 +675,22 @@ static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch
   st = check_ns(T, abc, kind, restart_mask);
   if (st != MNS_OK) return st;
   if (!aligned(X, 16) || !aligned(O, 16)) return MNS_ERR_PARAM;
-  const Store sto = dtype == MNS_BF16 ? Store::BF16 : Store::F32;
-  const Geo g = make_geo(rows, cols, sto);
-  const int cmax = batch < kChunk ? (int)batch : kChunk;
-  st = check_ws(ws, ws_bytes, ns_bytes(g, cmax, kind, rows, cols, nullptr, nullptr, nullptr, nullptr));
-  if (st != MNS_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return MNS_OK;
+}
+
+// The orthogonalisation of `batch` matrices in chunks of at most `cmax`, each chunk's
+// buffers carved from `ws` (split-k scratch capped at gemm_cap): per chunk the Frobenius
+// norm, the normalised iterate, T iterations (standard or Gram), and the export to O.
+static mns_status run_orthogonalize(const void* X, void* O, Store sto, const Geo& g,
+                                    int64_t batch, int64_t rows, int64_t cols, int T,
+                                    const float* abc, int kind, uint32_t restart_mask, void* ws,
+                                    int cmax, size_t gemm_cap, hipStream_t s) {
   const size_t esz = sto == Store::BF16 ? 2 : 4;
-  for (int64_t b0 = 0; b0 < batch; b0 += kChunk) {
-    const int c = (int)((batch - b0) < kChunk ? batch - b0 : kChunk);
+  for (int64_t b0 = 0; b0 < batch; b0 += cmax) {
+    const int c = (int)((batch - b0) < cmax ? batch - b0 : cmax);
     NsBuffers nb;
     float *partials = nullptr, *xscale = nullptr;
-    ns_bytes(g, c, kind, rows, cols, &nb, &partials, &xscale, ws);
+    ns_bytes(g, c, kind, rows, cols, &nb, &partials, &xscale, ws, gemm_cap);
     const bool km = kmajor_ns(g, c, nb);
     const char* xin = static_cast<const char*>(X) + (size_t)b0 * rows * cols * esz;
     char* out = static_cast<char*>(O) + (size_t)b0 * rows * cols * esz;
@@ -690,13 +704,95 @@ static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch
       return normalize(nullptr, xin, false, sto, c, rows, cols, xscale, g.elem,
                        straight(g, nb, km), transposed(g, nb, km), g.rows_p, g.cols_p, s); }));
     void* res = nullptr;
-    st = run_ns(g, c, nb, kind, T, abc, restart_mask, s, &res);
+    const mns_status st = run_ns(g, c, nb, kind, T, abc, restart_mask, s, &res);
     if (st != MNS_OK) return st;
     MNS_HIP(timed("export", 0, all * (ss + es), s, [&] {
       return export_output(res, g.elem, g.rows_p, g.cols_p, c, rows, cols, 1.0f / g.S, out,
                            sto, s); }));
   }
   return MNS_OK;
+}
+
+static mns_status orthogonalize(const void* X, void* O, int dtype, int64_t batch, int64_t rows,
+                                int64_t cols, int T, const float* abc, int kind,
+                                uint32_t restart_mask, void* ws, size_t ws_bytes, void* stream) {
+  mns_status st = check_orthogonalize(X, O, dtype, batch, rows, cols, T, abc, kind, restart_mask);
+  if (st != MNS_OK) return st;
+  const Store sto = dtype == MNS_BF16 ? Store::BF16 : Store::F32;
+  const Geo g = make_geo(rows, cols, sto);
+  const int cmax = batch < kChunk ? (int)batch : kChunk;
+  st = check_ws(ws, ws_bytes, ns_bytes(g, cmax, kind, rows, cols, nullptr, nullptr, nullptr, nullptr));
+  if (st != MNS_OK) return st;
+  return run_orthogonalize(X, O, sto, g, batch, rows, cols, T, abc, kind, restart_mask, ws, cmax,
+                           kGemmScratchBytes, static_cast<hipStream_t>(stream));
+}
+
+// ---- allocation-free standard NS (for callers that cannot allocate) ---------------------
+//
+// The same computation as ns_orthogonalize, with every buffer carved from one file-scope
+// device array instead of a caller workspace. Each GPU the library runs on holds its own
+// copy until the process ends. Host code never uses the array's name as an address: the
+// first call on a device looks up that device's copy with hipGetSymbolAddress (with the
+// device current) and keeps the pointer.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch` (looked up once per device).
+static mns_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MNS_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MNS_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MNS_OK;
+}
+
+// Matrices per chunk and split-k scratch cap so that one chunk's buffers fit in `scratch`:
+// the largest chunk (<= kChunk) whose buffers fit with the full split-k scratch of the
+// workspace path; else one matrix per chunk with what space remains for split-k parts.
+// False when one matrix's buffers alone do not fit.
+static bool noalloc_plan(const Geo& g, int64_t batch, int64_t rows, int64_t cols, int* cmax,
+                  size_t* gemm_cap) {
+  const int hi = batch < kChunk ? (int)batch : kChunk;
+  for (int c = hi; c >= 1; --c) {
+    if (ns_bytes(g, c, MNS_NS_STANDARD, rows, cols, nullptr, nullptr, nullptr, nullptr) <=
+        kNoAllocScratchBytes) {
+      *cmax = c;
+      *gemm_cap = kGemmScratchBytes;
+      return true;
+    }
+  }
+  const size_t base = ns_bytes(g, 1, MNS_NS_STANDARD, rows, cols, nullptr, nullptr, nullptr,
+                               nullptr, 0);
+  if (base > kNoAllocScratchBytes) return false;
+  *cmax = 1;
+  *gemm_cap = (kNoAllocScratchBytes - base) & ~size_t(255);
+  return true;
+}
+
+mns_status ns_orthogonalize_noalloc(const void* X, void* O, int dtype, int64_t batch,
+                                    int64_t rows, int64_t cols, int T, const float* abc,
+                                    void* stream) {
+  mns_status st = check_orthogonalize(X, O, dtype, batch, rows, cols, T, abc, MNS_NS_STANDARD, 0u);
+  if (st != MNS_OK) return st;
+  const Store sto = dtype == MNS_BF16 ? Store::BF16 : Store::F32;
+  const Geo g = make_geo(rows, cols, sto);
+  int cmax = 0;
+  size_t gemm_cap = 0;
+  if (!noalloc_plan(g, batch, rows, cols, &cmax, &gemm_cap)) return MNS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != MNS_OK) return st;
+  return run_orthogonalize(X, O, sto, g, batch, rows, cols, T, abc, MNS_NS_STANDARD, 0u, ws, cmax,
+                           gemm_cap, static_cast<hipStream_t>(stream));
 }
 
 mns_status ns_orthogonalize(const void* X, void* O, int dtype, int64_t batch, int64_t rows,

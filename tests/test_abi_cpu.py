@@ -163,3 +163,17 @@ def test_standalone_entry_points_validate(lib):
     fp = ctypes.POINTER(ctypes.c_float)
     assert lib.normuon_scale(0x1000, 1, 1, 8, 8, ctypes.cast(0x2000, fp), 2.0, 1e-8, 0x100000, 1 << 20, None) == _abi.MNS_ERR_PARAM
     assert lib.normuon_scale(0x1000, 1, 1, 8, 8, None, 0.9, 1e-8, 0x100000, 1 << 20, None) == _abi.MNS_ERR_NULL
+
+
+def test_noalloc_rejects_oversize_before_any_device_call(lib):
+    # 2304 x 4096 bf16 needs more than the 64 MiB device scratch for one matrix: the call
+    # must return MNS_ERR_WORKSPACE from the host checks alone (no device is touched here)
+    abc = (ctypes.c_float * 15)(*(list(QUINTIC) * 5))
+    assert lib.ns_orthogonalize_noalloc(0x1000, 0x200000, _abi.MNS_BF16, 1, 2304, 4096, 5, abc,
+                                        None) == _abi.MNS_ERR_WORKSPACE
+    assert lib.ns_orthogonalize_noalloc(0x1000, 0x200000, _abi.MNS_BF16, 1, 4096, 2304, 5, abc,
+                                        None) == _abi.MNS_ERR_WORKSPACE
+    # the usual argument checks come first
+    assert lib.ns_orthogonalize_noalloc(None, 0x2000, _abi.MNS_BF16, 1, 8, 8, 5, abc, None) == _abi.MNS_ERR_NULL
+    assert lib.ns_orthogonalize_noalloc(0x1000, 0x2000, 7, 1, 8, 8, 5, abc, None) == _abi.MNS_ERR_DTYPE
+    assert lib.ns_orthogonalize_noalloc(0x1000, 0x2000, _abi.MNS_BF16, 1, 8, 8, 0, abc, None) == _abi.MNS_ERR_PARAM
