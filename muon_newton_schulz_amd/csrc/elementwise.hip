@@ -327,6 +327,108 @@ __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* b
   }
 }
 
+// The straight layout alone (no transposed copy wanted: the products read X as stored): a
+// streaming pass, one thread per two 8-element vectors of the padded iterate (block-strided,
+// so a wave's loads and stores are contiguous), with non-temporal loads of the source and
+// stores of the iterate: each is touched once here, and the cache hints keep the stream from
+// displacing other lines (on this part the float32 -> float16 mix runs ~20 % faster so).
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+template <typename TS>
+__device__ __forceinline__ f8 load8_nt(const TS* p, int64_t i);
+template <>
+__device__ __forceinline__ f8 load8_nt<float>(const float* p, int64_t i) {
+  const f4v a = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p + i));
+  const f4v b = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p + i + 4));
+  return {make_float4(a.x, a.y, a.z, a.w), make_float4(b.x, b.y, b.z, b.w)};
+}
+template <>
+__device__ __forceinline__ f8 load8_nt<uint16_t>(const uint16_t* p, int64_t i) {
+  const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p + i));
+  return {make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                      bf16_to_f32(v.y >> 16)),
+          make_float4(bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xFFFFu),
+                      bf16_to_f32(v.w >> 16))};
+}
+
+template <typename TX>
+__device__ __forceinline__ void store8_nt(TX* p, int64_t i, const f8& v);
+template <>
+__device__ __forceinline__ void store8_nt<_Float16>(_Float16* p, int64_t i, const f8& v) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const h8 o = {(_Float16)v.lo.x, (_Float16)v.lo.y, (_Float16)v.lo.z, (_Float16)v.lo.w,
+                (_Float16)v.hi.x, (_Float16)v.hi.y, (_Float16)v.hi.z, (_Float16)v.hi.w};
+  __builtin_nontemporal_store(o, reinterpret_cast<h8*>(p + i));
+}
+template <>
+__device__ __forceinline__ void store8_nt<float>(float* p, int64_t i, const f8& v) {
+  const f4v a = {v.lo.x, v.lo.y, v.lo.z, v.lo.w}, b = {v.hi.x, v.hi.y, v.hi.z, v.hi.w};
+  __builtin_nontemporal_store(a, reinterpret_cast<f4v*>(p + i));
+  __builtin_nontemporal_store(b, reinterpret_cast<f4v*>(p + i + 4));
+}
+
+constexpr int kRowIter = 2;   // 8-element vectors per thread
+
+template <typename TS, typename TX, bool GATHER>
+__global__ __launch_bounds__(kThreads) void k_normalize_rows(PtrPack src, const TS* base,
+                                                             int64_t rows, int64_t cols,
+                                                             const float* xscale, TX* S,
+                                                             int64_t rows_p, int64_t cols_p,
+                                                             const int32_t* rowidx, float mu) {
+  const int b = blockIdx.y;
+  const TS* s = base ? base + (int64_t)b * rows * cols : static_cast<const TS*>(src.p[b]);
+  const int64_t lds = padded_ld(cols_p);
+  TX* so = S + (int64_t)b * rows_p * lds;
+  const float sc = xscale[b];
+  const int64_t vpr = cols_p / 8;                  // vectors per padded row
+  const int64_t nvec = rows_p * vpr;
+  const bool vec_ok = (cols % 8) == 0;
+  const int64_t v0 = (int64_t)blockIdx.x * kThreads * kRowIter + threadIdx.x;
+  f8 v[kRowIter];
+  int64_t dst[kRowIter];
+#pragma unroll
+  for (int it = 0; it < kRowIter; ++it) {
+    const int64_t vi = v0 + (int64_t)it * kThreads;
+    v[it] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    dst[it] = -1;
+    if (vi < nvec) {
+      const int64_t r = vi / vpr, c = 8 * (vi % vpr);
+      dst[it] = r * lds + c;
+      if (r < rows && c < cols) {
+        const int64_t sr = GATHER ? (int64_t)rowidx[(int64_t)b * rows + r] : r;
+        if (vec_ok) {
+          v[it] = load8_nt<TS>(s, sr * cols + c);
+          if constexpr (GATHER) {
+            const f8 w = v[it];
+            store8<float>(const_cast<float*>(s) + sr * cols, c,
+                          {make_float4(mu * w.lo.x, mu * w.lo.y, mu * w.lo.z, mu * w.lo.w),
+                           make_float4(mu * w.hi.x, mu * w.hi.y, mu * w.hi.z, mu * w.hi.w)});
+          }
+        } else {
+          float t8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            t8[e] = (c + e < cols) ? load1<TS>(s, sr * cols + c + e) : 0.f;
+            if constexpr (GATHER) {
+              if (c + e < cols) const_cast<float*>(s)[sr * cols + c + e] = mu * t8[e];
+            }
+          }
+          v[it] = {make_float4(t8[0], t8[1], t8[2], t8[3]), make_float4(t8[4], t8[5], t8[6], t8[7])};
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kRowIter; ++it) {
+    if (dst[it] < 0) continue;
+    f8 w = v[it];
+    w.lo.x *= sc; w.lo.y *= sc; w.lo.z *= sc; w.lo.w *= sc;
+    w.hi.x *= sc; w.hi.y *= sc; w.hi.z *= sc; w.hi.w *= sc;
+    store8_nt<TX>(so, dst[it], w);
+  }
+}
+
 // ---- O (caller layout) = inv_s * iterate in the stored layout ------------------------------
 
 template <typename TX, typename TO>
@@ -451,8 +553,9 @@ __global__ __launch_bounds__(kThreads) void k_fill(float* p, int64_t n, float va
 
 // ---- a7: fused weight update W <- W - lr * rowscale_i * O_ij, one rounding ------------------
 
-// Each thread updates 8 consecutive columns of kWuRows rows (all loads issued first).
-constexpr int kWuRows = 4;
+// Each thread updates 8 consecutive columns of kWuRows rows (all loads issued first); one row
+// per thread, one block row per matrix row, measured fastest (a one-shot grid).
+constexpr int kWuRows = 1;
 
 template <typename TW, typename TX>
 __global__ __launch_bounds__(kThreads) void k_wupdate(PtrPack Wp, int64_t rows, int64_t cols,
@@ -732,6 +835,16 @@ static void launch_normalize(const PtrPack* pack, const void* base, int count, i
                              float mu = 0.f) {
   PtrPack pk = {};
   if (pack) pk = *pack;
+  if (!T) {
+    // straight layout only: the streaming pass
+    const int64_t nvec = rows_p * (cols_p / 8);
+    const int64_t per = (int64_t)kThreads * kRowIter;
+    dim3 grid1((unsigned)((nvec + per - 1) / per), count);
+    hipLaunchKernelGGL((k_normalize_rows<TS, TX, GATHER>), grid1, dim3(kThreads), 0, s, pk,
+                       static_cast<const TS*>(base), rows, cols, xscale, static_cast<TX*>(S),
+                       rows_p, cols_p, rowidx, mu);
+    return;
+  }
   dim3 grid((unsigned)(cols_p / kNormCols), (unsigned)(rows_p / kNormRows), count);
   hipLaunchKernelGGL((k_normalize<TS, TX, GATHER>), grid, dim3(kThreads), 0, s, pk,
                      static_cast<const TS*>(base), rows, cols, xscale, static_cast<TX*>(S),
