@@ -15,6 +15,8 @@ default workload is the largest: the 196-matrix layer set of a 3B-like transform
     buffer written before each launch (the 256 MB Infinity Cache evicted);
   * ns_gate_4096x16384: the 4096x16384 bf16 standard-NS step timed in the same process, its
     Newton-Schulz GEMM phase as a fraction of the bf16 MFMA peak;
+  * gram_ns_same_matrices: the step with Gram Newton-Schulz (restart before iteration 3) on
+    the same resident matrices, and its speedup over the standard-NS step;
   * cpu_baseline: the fp64 oracle on a bounded sample, on the host's cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {1..7}] [--kind standard|gram]
@@ -59,6 +61,8 @@ def parse(argv=None):
                     help="skip the 4096x16384 standard-NS gate timing")
     ap.add_argument("--no-flush-pass", action="store_true",
                     help="skip the cache-flushed timing of the HBM kernels")
+    ap.add_argument("--no-gram", action="store_true",
+                    help="skip the Gram NS timing on the same matrices")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args(argv)
@@ -407,6 +411,37 @@ def main(argv=None):
         flushed = kernel_table(big, 0, peak)   # the launches that moved >= 16 MiB (flushed ones)
         flushed = {"steps": n_fl, "flush_bytes": FLUSH_BYTES, "gate": HBM_GATE, "kernels": flushed}
 
+    # The page's Gram Newton-Schulz (Theorem 2, restart before iteration 3) on the same resident
+    # matrices, for comparison with the standard NS timed above (fewer algorithmic FLOPs).
+    gram = None
+    if not args.no_gram and kind == "standard" and wl.n_matrices > 1:
+        say("Gram NS on the same matrices")
+        gkw = dict(work.kw, kind="gram", restart_before=(3,))
+        gws = torch.empty(mns.step_workspace_size(work.W, work.M, work.G, work.v_arg, **gkw),
+                          dtype=torch.uint8, device=dev)
+
+        def gstep():
+            mns.muon_step(work.W, work.M, work.G, work.v_arg, workspace=gws, stream=work.stream, **gkw)
+
+        for _ in range(args.warmup):
+            gstep()
+        mns.profile_begin()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(work.stream)
+        for _ in range(args.steps):
+            gstep()
+        g1.record(work.stream)
+        torch.cuda.synchronize()
+        gstats = mns.profile_end()
+        g_ms = g0.elapsed_time(g1) / args.steps
+        g_flops, g_ns_ms = gemm_phase(gstats, args.steps)
+        gram = {"ns": "gram", "restart_before": [3], "ms_per_step": round(g_ms, 4),
+                "ns_flops_per_step": g_flops,
+                "ns_gemm_tflops": round(g_flops / (g_ns_ms * 1e-3) / 1e12, 1),
+                "step_speedup_vs_standard": round(ms_step / g_ms, 3)}
+        del gws
+
     graph = None
     if not args.no_graph:
         say("graph replay")
@@ -469,6 +504,7 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": cpu,
         "ns_gate_4096x16384": gate,
+        "gram_ns_same_matrices": gram,
         "hbm_kernels_cache_flushed": flushed,
         "graph": graph,
         "kernels": kernels,
