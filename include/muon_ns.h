@@ -162,6 +162,8 @@ mns_status gram_ns_orthogonalize(const void* X, void* O, int dtype, int64_t batc
  *   to e.g. 2048 x 2048 or 1024 x 4096) returns MNS_ERR_WORKSPACE before anything is enqueued.
  *   Other arguments and errors as ns_orthogonalize; the result equals its result up to the
  *   order of split-k partial sums (bit-identical when the chunking and split-k scratch agree).
+ *   Device: the array used is the current device's; `stream` (if not NULL) must belong to
+ *   the current device, else MNS_ERR_PARAM.
  *   Concurrency: every call on one GPU uses that GPU's single array, which keeps the last
  *   call's contents (each call writes every word before reading it). Calls that may overlap
  *   on one GPU -- on different streams, or from different threads -- race; serialise them. */

@@ -741,10 +741,16 @@ static constexpr int kMaxDevices = 64;
 static std::mutex g_scratch_mu;
 static void* g_scratch_ptr[kMaxDevices] = {};
 
-// This device's copy of `scratch` (looked up once per device).
-static mns_status scratch_on_current_device(void** out) {
+// This device's copy of `scratch` (looked up once per device). The stream, if given, must
+// belong to the current device: the array's address is the current device's.
+static mns_status scratch_on_current_device(hipStream_t stream, void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MNS_ERR_HIP;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MNS_ERR_HIP;
+    if (sdev != dev) return MNS_ERR_PARAM;
+  }
   std::lock_guard<std::mutex> lk(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void* p = nullptr;
@@ -789,7 +795,7 @@ mns_status ns_orthogonalize_noalloc(const void* X, void* O, int dtype, int64_t b
   size_t gemm_cap = 0;
   if (!noalloc_plan(g, batch, rows, cols, &cmax, &gemm_cap)) return MNS_ERR_WORKSPACE;
   void* ws = nullptr;
-  st = scratch_on_current_device(&ws);
+  st = scratch_on_current_device(static_cast<hipStream_t>(stream), &ws);
   if (st != MNS_OK) return st;
   return run_orthogonalize(X, O, sto, g, batch, rows, cols, T, abc, MNS_NS_STANDARD, 0u, ws, cmax,
                            gemm_cap, static_cast<hipStream_t>(stream));
