@@ -17,6 +17,7 @@ default workload is the largest: the 196-matrix layer set of a 3B-like transform
     Newton-Schulz GEMM phase as a fraction of the bf16 MFMA peak;
   * gram_ns_same_matrices: the step with Gram Newton-Schulz (restart before iteration 3) on
     the same resident matrices, and its speedup over the standard-NS step;
+  * gpu_clocks: the graphics and memory clocks (and socket power) read during the timed steps;
   * cpu_baseline: the fp64 oracle on a bounded sample, on the host's cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {1..7}] [--kind standard|gram]
@@ -36,6 +37,7 @@ if ROOT not in sys.path:
 # MI355X published peaks (dense MFMA and HBM3E)
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0       # the clock the published MFMA peaks are quoted at
 DEFAULT_WORKLOAD = 4          # the 196-matrix layer set (the largest workload)
 GATE_WORKLOAD = 3             # 4096x16384 bf16, standard NS: the MFMA gate (>= 60 % of peak)
 MFMA_GATE = 0.60
@@ -287,6 +289,55 @@ def kernel_table(stats, total_ms, peak):
     return kernels
 
 
+class ClockSampler:
+    """The GPU's graphics (SYS) and memory clocks and its socket power, read through amdsmi
+    while timed work drains (the clock this part sustains under MFMA load is well below the
+    2.4 GHz of the published peak). Every field is None where the library or the reading is
+    unavailable."""
+
+    def __init__(self):
+        self.h = None
+        self.sys, self.mem, self.power = [], [], []
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if len(hs) == 1:
+                self.amdsmi, self.h = amdsmi, hs[0]
+        except Exception:
+            self.h = None
+
+    def sample(self):
+        if self.h is None:
+            return
+        a = self.amdsmi
+        try:
+            self.sys.append(a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.SYS)["clk"])
+            self.mem.append(a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.MEM)["clk"])
+        except Exception:
+            pass
+        try:
+            pw = a.amdsmi_get_power_info(self.h)
+            w = pw.get("current_socket_power") or pw.get("average_socket_power")
+            if isinstance(w, (int, float)):
+                self.power.append(float(w))
+        except Exception:
+            pass
+
+    def summary(self):
+        def stats(v):
+            v = [x for x in v if isinstance(x, (int, float))]
+            return {"mean": round(sum(v) / len(v), 1), "min": min(v), "max": max(v)} if v else None
+        out = {"sys_clock_mhz": stats(self.sys), "mem_clock_mhz": stats(self.mem),
+               "socket_power_w": stats(self.power), "samples": len(self.sys),
+               "source": "amdsmi" if self.h is not None else None}
+        # context: the published dense peak assumes 2.4 GHz; the peak at the clock held here
+        if out["sys_clock_mhz"]:
+            out["f16_peak_tflops_at_mean_clock"] = round(
+                PEAK_TFLOPS["f16"] * out["sys_clock_mhz"]["mean"] / PEAK_CLOCK_MHZ, 1)
+        return out
+
+
 class Workload:
     """One workload resident on the GPU, with its step arguments and workspace."""
 
@@ -308,10 +359,11 @@ class Workload:
         self.mns.muon_step(self.W, self.M, self.G, self.v_arg, workspace=self.ws,
                            stream=self.stream, **self.kw)
 
-    def run(self, steps, profile=False, flush=None):
+    def run(self, steps, profile=False, flush=None, clocks=None):
         """`steps` steps between two synchronisations; returns (ms per step, kernel stats or
         None). With `profile` the library records a hipEvent pair around each launch; with
-        `flush` (a device buffer) it writes over it before each HBM-bound launch."""
+        `flush` (a device buffer) it writes over it before each HBM-bound launch; with `clocks`
+        (a ClockSampler) the clocks are read every few milliseconds until the steps are done."""
         torch = self.torch
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if profile:
@@ -323,6 +375,10 @@ class Workload:
         for _ in range(steps):
             self.step()
         e1.record(self.stream)
+        if clocks is not None:
+            while not e1.query():
+                clocks.sample()
+                time.sleep(0.005)
         torch.cuda.synchronize()
         stats = self.mns.profile_end() if profile else None
         return e0.elapsed_time(e1) / steps, stats
@@ -371,7 +427,8 @@ def main(argv=None):
 
     # The timed steps, with the per-launch events (the roofline's source).
     say(f"timing {args.steps} steps")
-    ms_step, stats = work.run(args.steps, profile=True)
+    clocks = ClockSampler()
+    ms_step, stats = work.run(args.steps, profile=True, clocks=clocks)
     total_ms = ms_step * args.steps
     ns_flops, ns_ms = gemm_phase(stats, args.steps)
     value = ns_flops / (ms_step * 1e-3) / 1e12
@@ -458,7 +515,8 @@ def main(argv=None):
         say(f"gate workload: {gwl.name}, standard NS")
         gw = Workload(gwl, "standard", torch, np, mns, synthetic, dev)
         gw.run(args.warmup)
-        g_ms, g_stats = gw.run(args.steps, profile=True)
+        gclocks = ClockSampler()
+        g_ms, g_stats = gw.run(args.steps, profile=True, clocks=gclocks)
         g_flops, g_ns_ms = gemm_phase(g_stats, args.steps)
         g_plain, _ = gw.run(args.steps)
         gate_tf = g_flops / (g_ns_ms * 1e-3) / 1e12
@@ -468,6 +526,7 @@ def main(argv=None):
                 "ns_gemm_frac": round(gate_tf / PEAK_TFLOPS["f16"], 4), "gate": MFMA_GATE,
                 "step_tflops": round(g_flops / (g_ms * 1e-3) / 1e12, 1),
                 "dense_equivalent_tflops": round(dense_equivalent_flops(gwl) / (g_ms * 1e-3) / 1e12, 1),
+                "gpu_clocks": gclocks.summary(),
                 "kernels": kernel_table(g_stats, g_ms * args.steps, PEAK_TFLOPS["f16"])}
         gw.free()
         del gw
@@ -502,6 +561,7 @@ def main(argv=None):
         "dense_equivalent_tflops": round(dense_eq / (ms_step * 1e-3) / 1e12, 1) if dense_eq else None,
         "mfma_frac_step": round(value / peak, 4),
         "roofline": roof,
+        "gpu_clocks": clocks.summary(),
         "cpu_baseline": cpu,
         "ns_gate_4096x16384": gate,
         "gram_ns_same_matrices": gram,

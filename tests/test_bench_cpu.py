@@ -75,3 +75,10 @@ def test_host_info_fields():
     info, threads = bench.host_info()
     assert info["os_cpu_count"] == os.cpu_count()
     assert "cpu_model" in info and "blas" in info
+
+
+def test_clock_sampler_reports_fields_without_a_device():
+    c = bench.ClockSampler()
+    c.sample()
+    s = c.summary()
+    assert set(s) == {"sys_clock_mhz", "mem_clock_mhz", "socket_power_w", "samples", "source"}

@@ -61,5 +61,6 @@ def test_bench_line_with_gate_and_gram():
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
     assert cpu["os_cpu_count"] >= 1
+    assert "sys_clock_mhz" in d["gpu_clocks"]
     flushed = d["hbm_kernels_cache_flushed"]["kernels"]
     assert "momentum" in flushed and 0 < flushed["momentum"]["frac"] < 1
