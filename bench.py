@@ -295,12 +295,23 @@ class ClockSampler:
     2.4 GHz of the published peak). Every field is None where the library or the reading is
     unavailable."""
 
+    _lib = None          # amdsmi, initialised once per process (shut down at exit)
+
+    @classmethod
+    def _amdsmi(cls):
+        if cls._lib is None:
+            import atexit
+            import amdsmi
+            amdsmi.amdsmi_init()
+            atexit.register(amdsmi.amdsmi_shut_down)
+            cls._lib = amdsmi
+        return cls._lib
+
     def __init__(self):
         self.h = None
         self.sys, self.mem, self.power = [], [], []
         try:
-            import amdsmi
-            amdsmi.amdsmi_init()
+            amdsmi = self._amdsmi()
             hs = amdsmi.amdsmi_get_processor_handles()
             if len(hs) == 1:
                 self.amdsmi, self.h = amdsmi, hs[0]
