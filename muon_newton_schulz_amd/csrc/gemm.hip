@@ -41,10 +41,12 @@
 //     k-step of k-tile k+1, so it has most of a k-tile to land before the next barrier.
 //   * MFMA operand roles are swapped (the B tile feeds the MFMA's A input), so each lane's
 //     accumulators hold 4 consecutive output columns of one row.
-//   * The epilogue stages the finished tile in the (then idle) LDS and writes every output
-//     as 16-byte row chunks: [m][n] for C, [n][m] for C^T and for the mirrored tile. On
-//     request the pass that writes the stored layout also sums the squares of each output
-//     row per 64-column chunk (NorMuon's row statistics, Eq. (2)), from the values as stored.
+//   * The epilogue stages the finished tile once in the (then idle) LDS, as [m][n], and
+//     writes every output as 16-byte row chunks: C from its rows, C^T and the mirrored tile
+//     from its columns through the transposing LDS read (4 rows x 16 columns per 16 lanes
+//     become 16 columns of 4). On request the pass that writes the stored layout also sums
+//     the squares of each output row per 64-column chunk (NorMuon's row statistics, Eq. (2)),
+//     from the values as stored.
 //   * Work decomposition: whole rounds of tiles (one block per tile, one round = one block
 //     per CU slot); when the last round would be less than half full, its tiles are split
 //     along k so that round is full. Split blocks write float32 partial sums; a later launch
