@@ -39,6 +39,11 @@
 //     instructions at 256x256) goes out in two halves, one instruction after each of the
 //     first MFMAs of the last k-step of k-tile k (just after its barrier) and of the first
 //     k-step of k-tile k+1, so it has most of a k-tile to land before the next barrier.
+//   * A diagonal tile of a symmetric product whose two operands are one matrix (X X^T, A A)
+//     loads only its A k-tiles and reads the B fragments from them, and skips the MFMAs of the
+//     fragments wholly below the diagonal (that part of a diagonal tile is never stored); the
+//     waves take the tile's regions in an order that leaves each SIMD at most 10 of its 16
+//     fragments. Results are bit-identical to the full tile's.
 //   * MFMA operand roles are swapped (the B tile feeds the MFMA's A input), so each lane's
 //     accumulators hold 4 consecutive output columns of one row.
 //   * The epilogue stages the finished tile once in the (then idle) LDS, as [m][n], and
@@ -206,7 +211,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS-DMA bases stay scalar
-  const int wm = wave / WGN, wn = wave % WGN;
 
   // Block -> (tile, k-range, partial slot); see the work decomposition above.
   // Tile order. Workgroups go round-robin to the 8 XCDs (L2 domains); whole-tile blocks are
@@ -274,6 +278,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rB =
       make_rsrc(Bbase, (KB ? (int64_t)p.K * p.ldb - n0 : (int64_t)(p.N - n0) * p.ldb) * ES);
 
+  // A diagonal tile of a symmetric product whose operands are one matrix (X X^T, A A): its A
+  // and B k-tiles are the same rows, so only A is loaded and the B fragments are read from the
+  // A stage; fragments wholly below the diagonal are never stored (the row pass keeps the upper
+  // triangle, the mirror is made from it), so their MFMAs are skipped. Waves get the 128 x 64
+  // regions in a permuted order that pairs, on each SIMD (waves w and w + 4), a region with
+  // much of the upper triangle and one with little: at most 10 of 16 fragments per SIMD.
+  constexpr bool kDiagOK = SYM && !KB && BM == 256 && BN == 256 && WGM == 2 && WGN == 4;
+  const bool diag_same = kDiagOK && slot < 0 && tm == tn && p.A == p.B && p.sA == p.sB &&
+                         p.lda == p.ldb;
+  const int reg = diag_same ? (int)((0x06547132u >> (4 * wave)) & 0xFu) : wave;
+  const int wm = reg / WGN, wn = reg % WGN;
+  uint32_t keep = 0u;   // bit m: fragment (m / FN, m % FN) of this wave is on or above the diagonal
+#pragma unroll
+  for (int m = 0; m < FM * FN; ++m)
+    keep |= (uint32_t)(wm * FM + m / FN <= wn * FN + m % FN) << m;
+  keep = __builtin_amdgcn_readfirstlane(keep);
+
   // Lane -> (LDS row, physical chunk) of one DMA instruction: row r0 + lane/8, chunk
   // lane%8, which holds logical k-chunk (lane%8) ^ f(row).
   int offA[A_INST], offB[B_INST];
@@ -301,15 +322,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   // k offset of k-tile kt in the B rows (bytes, scalar)
   auto b_koff = [&](int kt) { return KB ? kt * BK * (int)p.ldb * ES : kt * BK * ES; };
 
-  auto issue = [&](int kt, int buf) {
+  auto issue = [&](int kt, int buf, auto dg) {
     const int so = kt * BK * ES;
 #pragma unroll
     for (int i = 0; i < A_INST; ++i)
       dma16(rA, &lds[buf * STAGE + (wave * A_INST + i) * 8 * kChunks], offA[i], so);
+    if constexpr (!decltype(dg)::value) {
 #pragma unroll
-    for (int i = 0; i < B_INST; ++i)
-      dma16(rB, &lds[buf * STAGE + (BM + (wave * B_INST + i) * 8) * kChunks], offB[i],
-            b_koff(kt));
+      for (int i = 0; i < B_INST; ++i)
+        dma16(rB, &lds[buf * STAGE + (BM + (wave * B_INST + i) * 8) * kChunks], offB[i],
+              b_koff(kt));
+    }
   };
 
   floatx16 acc[FM][FN];
@@ -321,7 +344,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int arow = wm * WM + (lane & 31);
-  const int brow = BM + wn * WN + (lane & 31);
+  const int brow = (diag_same ? 0 : BM) + wn * WN + (lane & 31);
   u32x4 af[2][FM], bf[2][FN];
   auto load_frags = [&](int buf, int ks, int slot) {
     const int ch = 2 * ks + (lane >> 5);
@@ -392,8 +415,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     // DMA instruction q of a k-tile (q < A_INST: A row block q, else B row block q - A_INST).
     constexpr int NI = A_INST + B_INST;
     constexpr int NP0 = NI / 2, NP1 = NI - NP0;
-    auto dma_one = [&](int kt, int buf, int q) {
+    auto dma_one = [&](int kt, int buf, int q, auto dg) {
       const int so = kt * BK * ES;
+      if (decltype(dg)::value && q >= A_INST) return;
       if (q < A_INST)
         dma16(rA, &lds[buf * STAGE + (wave * A_INST + q) * 8 * kChunks], offA[q], so);
       else
@@ -402,21 +426,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     };
     // One k-step: the MFMAs of fragment slot s with DMA instructions q0 .. q0+nq-1 of k-tile
     // kt spread between them (after every RR-th MFMA).
-    auto kstep = [&](int s, int kt, int buf, int q0, auto nq_c) {
+    auto kstep = [&](int s, int kt, int buf, int q0, auto nq_c, auto dg) {
       constexpr int NQ = decltype(nq_c)::value;
+      constexpr bool DG = decltype(dg)::value;
       constexpr int NM = FM * FN;
       constexpr int RR = NM / (NQ + 1) > 0 ? NM / (NQ + 1) : 1;
       // DMA instruction q goes out after MFMA pos(q) = min((q + 1) RR, NM) - 1.
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        Tr::mma(acc[m / FN][m % FN], bf[s][m % FN], af[s][m / FN]);
+        if (!DG || ((keep >> m) & 1u)) Tr::mma(acc[m / FN][m % FN], bf[s][m % FN], af[s][m / FN]);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           const int pos = (q + 1) * RR < NM ? (q + 1) * RR - 1 : NM - 1;
-          if (pos == m) dma_one(kt, buf, q0 + q);
+          if (pos == m) dma_one(kt, buf, q0 + q, dg);
         }
       }
-      if constexpr (true && NQ > 0) {
+      if constexpr (!DG && NQ > 0) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -435,50 +460,58 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     // out in the previous k-tile's last k-step, its second half goes out during k-step 0
     // here; the barrier before k-step 3 waits for it, and the first half of k-tile kl+2
     // follows the barrier.
-    auto body = [&](int kl, auto has1, auto has2) {
+    auto body = [&](int kl, auto has1, auto has2, auto dg) {
       const int b = kl & 1;
       // This k-tile's first fragments were read a whole k-step ago: waiting for them here is
       // free and leaves only the next k-step's reads pending below.
       __builtin_amdgcn_s_waitcnt(0xC07F);
       load_frags(b, 1, 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(has1)::value) kstep(0, k_begin + kl + 1, b ^ 1, NP0, IP1{});
-      else kstep(0, 0, 0, 0, I0{});
+      if constexpr (decltype(has1)::value) kstep(0, k_begin + kl + 1, b ^ 1, NP0, IP1{}, dg);
+      else kstep(0, 0, 0, 0, I0{}, dg);
       __builtin_amdgcn_sched_barrier(0);
       load_b(b, 1, 1);
       load_frags(b, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
-      kstep(1, 0, 0, 0, I0{});
+      kstep(1, 0, 0, 0, I0{}, dg);
       __builtin_amdgcn_sched_barrier(0);
       load_b(b, 2, 0);
       load_frags(b, 3, 1);
       __builtin_amdgcn_sched_barrier(0);
-      kstep(0, 0, 0, 0, I0{});
+      kstep(0, 0, 0, 0, I0{}, dg);
       __builtin_amdgcn_sched_barrier(0);
       load_b(b, 3, 1);
       // k-tile kl+1 has landed and every wave's reads of buffer b are done.
       block_sync();
       load_frags(b ^ 1, 0, 0);   // after the last k-tile: a harmless read of the idle buffer
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(has2)::value) kstep(1, k_begin + kl + 2, b, 0, IP0{});
-      else kstep(1, 0, 0, 0, I0{});
+      if constexpr (decltype(has2)::value) kstep(1, k_begin + kl + 2, b, 0, IP0{}, dg);
+      else kstep(1, 0, 0, 0, I0{}, dg);
       __builtin_amdgcn_sched_barrier(0);
       load_b(b ^ 1, 0, 0);   // after the last k-tile: a harmless read of the idle buffer
     };
     using T1 = std::true_type;
     using F1 = std::false_type;
-    issue(k_begin, 0);
-    if (KL > 1) {
+    auto run = [&](auto dg) {
+      issue(k_begin, 0, dg);
+      if (KL > 1) {
 #pragma unroll
-      for (int q = 0; q < NP0; ++q) dma_one(k_begin + 1, 1, q);
+        for (int q = 0; q < NP0; ++q) dma_one(k_begin + 1, 1, q, dg);
+      }
+      block_sync();
+      load_frags(0, 0, 0);
+      load_b(0, 0, 0);
+      int kl = 0;
+      for (; kl + 2 < KL; ++kl) body(kl, T1{}, T1{}, dg);
+      if (kl + 1 < KL) body(kl++, T1{}, F1{}, dg);
+      body(kl, F1{}, F1{}, dg);
+    };
+    if constexpr (kDiagOK) {
+      if (diag_same) run(T1{});
+      else run(F1{});
+    } else {
+      run(F1{});
     }
-    block_sync();
-    load_frags(0, 0, 0);
-    load_b(0, 0, 0);
-    int kl = 0;
-    for (; kl + 2 < KL; ++kl) body(kl, T1{}, T1{});
-    if (kl + 1 < KL) body(kl++, T1{}, F1{});
-    body(kl, F1{}, F1{});
     if (slot >= 0) {
       floatx4* P = reinterpret_cast<floatx4*>(p.partial) + (int64_t)slot * TILE_F4;
 #pragma unroll
