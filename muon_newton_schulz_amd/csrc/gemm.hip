@@ -287,6 +287,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   constexpr bool kDiagOK = SYM && !KB && BM == 256 && BN == 256 && WGM == 2 && WGN == 4;
   const bool diag_same = kDiagOK && slot < 0 && tm == tn && p.A == p.B && p.sA == p.sB &&
                          p.lda == p.ldb;
+  // Region r = wm * WGN + wn; wave w takes nibble w of 0x06547132 (waves 0-3: regions 2, 3, 1, 7
+  // with 8, 8, 7, 7 fragments on or above the diagonal; waves 4-7: regions 4, 5, 6, 0 with
+  // 0, 0, 3, 3).
   const int reg = diag_same ? (int)((0x06547132u >> (4 * wave)) & 0xFu) : wave;
   const int wm = reg / WGN, wn = reg % WGN;
   uint32_t keep = 0u;   // bit m: fragment (m / FN, m % FN) of this wave is on or above the diagonal
