@@ -177,3 +177,28 @@ def test_noalloc_rejects_oversize_before_any_device_call(lib):
     assert lib.ns_orthogonalize_noalloc(None, 0x2000, _abi.MNS_BF16, 1, 8, 8, 5, abc, None) == _abi.MNS_ERR_NULL
     assert lib.ns_orthogonalize_noalloc(0x1000, 0x2000, 7, 1, 8, 8, 5, abc, None) == _abi.MNS_ERR_DTYPE
     assert lib.ns_orthogonalize_noalloc(0x1000, 0x2000, _abi.MNS_BF16, 1, 8, 8, 0, abc, None) == _abi.MNS_ERR_PARAM
+
+
+def test_profile_session_states(lib):
+    """The instrumentation calls outside and inside a session: with nothing launched in it, a
+    session makes no device call, so the state rules are checked here."""
+    n = ctypes.c_int(-1)
+    stats = (_abi.MnsKernelStat * 4)()
+    # no session open
+    assert lib.mns_profile_set_flush(None, 0) == _abi.MNS_ERR_PARAM
+    assert lib.mns_profile_end(stats, 4, ctypes.byref(n)) == _abi.MNS_ERR_PARAM
+    assert lib.mns_profile_begin() == _abi.MNS_OK
+    try:
+        # a flush buffer must be 16-byte aligned; NULL or zero bytes turns the flush off
+        assert lib.mns_profile_set_flush(ctypes.c_void_p(0x10008), 1 << 30) == _abi.MNS_ERR_PARAM
+        assert lib.mns_profile_set_flush(ctypes.c_void_p(0x10000), 1 << 30) == _abi.MNS_OK
+        assert lib.mns_profile_set_flush(None, 0) == _abi.MNS_OK
+        assert lib.mns_profile_set_flush(ctypes.c_void_p(0x10000), 0) == _abi.MNS_OK
+        # a second begin restarts the session
+        assert lib.mns_profile_begin() == _abi.MNS_OK
+    finally:
+        assert lib.mns_profile_end(stats, 4, ctypes.byref(n)) == _abi.MNS_OK
+    assert n.value == 0   # nothing was launched in the session
+    # end closes it, and turns the flush off with it
+    assert lib.mns_profile_end(stats, 4, ctypes.byref(n)) == _abi.MNS_ERR_PARAM
+    assert lib.mns_profile_set_flush(ctypes.c_void_p(0x10000), 1 << 30) == _abi.MNS_ERR_PARAM
