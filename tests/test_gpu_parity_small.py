@@ -249,3 +249,56 @@ def test_repeat_runs_are_bitwise_identical():
     d = mns.gram_ns_orthogonalize(X, [QUINTIC] * 5)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(c, d)
+
+
+@pytest.mark.parametrize("kind,f", [("standard", 1.0), ("gram", 1.0), ("standard", 0.25)])
+def test_zero_matrices_among_others(kind, f):
+    """Matrices whose momentum and gradient are zero, batched with non-zero ones of the same
+    shape: each matrix has its own scale in the one launch sequence, so the zero ones keep W
+    bit for bit and M at zero, with v decayed by beta2 (their NorMuon ratio is 0/0, taken as
+    0), and the others still match the oracle (standard NS, Gram NS, Dion3 rows)."""
+    _say("case zero among others", kind, f)
+    shapes = [(300, 700)] * 4
+    zero = {1, 3}
+    mu, lr, beta2 = 0.9, 0.05, 0.9
+    Ws = [synthetic.weight(r, c, "bf16", 960, i) for i, (r, c) in enumerate(shapes)]
+    Ms = [np.zeros((r, c)) if i in zero else synthetic.state(r, c, 960, i, scale=0.5)
+          for i, (r, c) in enumerate(shapes)]
+    # bfloat16 storage: the gradients are bit patterns (0x0000 is +0.0)
+    Gs = [np.zeros((r, c), dtype=np.uint16) if i in zero
+          else synthetic.gradient("student_t", r, c, "bf16", 961, 0, i)
+          for i, (r, c) in enumerate(shapes)]
+    vs = [np.abs(synthetic.state(r, 1, 962, i, scale=0.01)).reshape(r) for i, (r, c) in enumerate(shapes)]
+    W = [to_device(w, "bf16") for w in Ws]
+    M = [torch.from_numpy(m).float().cuda() for m in Ms]
+    v = [torch.from_numpy(x.astype(np.float32)).cuda() for x in vs]
+    W_before = [to_f64(t) for t in W]
+    W_bits = [t.clone() for t in W]
+    v_before = [to_f64(t) for t in v]
+    mns.muon_step(W, M, [to_device(g, "bf16") for g in Gs], v, mu=mu, lr=lr,
+                  coeffs=[QUINTIC] * 5, kind=kind, restart_before=(3,) if kind == "gram" else (),
+                  normuon=True, beta2=beta2, eps=1e-8, row_fraction=f)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.isfinite(W[i].float()).all() and torch.isfinite(v[i]).all(), f"non-finite [{i}]"
+        if i in zero:
+            assert torch.equal(W[i], W_bits[i]), f"W[{i}] changed"
+            assert not M[i].any(), f"M[{i}] not zero"
+            # rows of the zero matrix: v <- beta2 v (every row, or the selected rows for Dion3)
+            vv = to_f64(v[i])
+            decayed = np.isclose(vv, beta2 * v_before[i], rtol=1e-6, atol=0)
+            kept = np.isclose(vv, v_before[i], rtol=0, atol=0)
+            assert decayed.all() if f == 1.0 else (decayed | kept).all(), f"v[{i}]"
+            continue
+        g64 = stored_f64(Gs[i], "bf16")
+        kw = dict(coeffs=[QUINTIC] * 5, kind=kind, restart_before=(3,) if kind == "gram" else (),
+                  normuon=True, v=v_before[i], beta2=beta2, eps=1e-8, storage="bf16")
+        if f < 1.0:
+            ref = oracle.dion3_step(W_before[i], np.asarray(Ms[i], dtype=np.float64), g64, mu=mu,
+                                    lr=lr, f=f, **kw)
+        else:
+            ref = oracle.muon_step(W_before[i], np.asarray(Ms[i], dtype=np.float64), g64, mu=mu,
+                                   lr=lr, **kw)
+        check_weight(to_f64(W[i]), W_before[i], ref["W_exact"] - W_before[i], "bf16", f"W[{i}]")
+        assert rel(to_f64(M[i]), ref["M"]) < 1e-6, f"M[{i}]"
+        assert rel(to_f64(v[i]), ref["v"]) < TOL["bf16"], f"v[{i}]"
