@@ -477,14 +477,14 @@ mns_status validate_step(const mns_matrix* mats, int count, const mns_hparams* h
 
 // Workspace layout of one chunk (<= kChunk matrices of one shape) of muon_step.
 struct StepWs {
-  float* partials = nullptr;
+  double* partials = nullptr;
   float* xscale = nullptr;
   NsBuffers ns;
   float* part = nullptr;
   float* rowscale = nullptr;
   double* fin = nullptr;
   float* l1 = nullptr;
-  float* l2sq = nullptr;
+  double* l2sq = nullptr;
   int32_t* S = nullptr;
   int nblk = 0, chunks = 0;
 };
@@ -493,7 +493,7 @@ size_t carve_step(void* base, const Geo& g, int count, int64_t rows, int64_t col
                   int64_t k, int kind, StepWs& w) {
   Carver cv(base);
   w.nblk = dion ? 0 : norm_blocks(rows * cols);
-  w.partials = cv.take<float>((size_t)count * w.nblk);
+  w.partials = cv.take<double>((size_t)count * w.nblk);
   w.xscale = cv.take<float>((size_t)count);
   carve_ns(cv, g, count, kind, w.ns);
   w.chunks = (int)(g.cols_p / 64);                     // row-norm partials per stored row
@@ -503,7 +503,7 @@ size_t carve_step(void* base, const Geo& g, int count, int64_t rows, int64_t col
   if (dion) {
     w.l1 = cv.take<float>((size_t)count * rows);
     w.S = cv.take<int32_t>((size_t)count * k);
-    w.l2sq = cv.take<float>((size_t)count * rows);
+    w.l2sq = cv.take<double>((size_t)count * rows);
   }
   return cv.off + 256;
 }
@@ -632,12 +632,12 @@ mns_status muon_step(const mns_matrix* mats, int count, const mns_hparams* hp, v
 // ---- standalone orthogonalisation ------------------------------------------------------------
 
 static size_t ns_bytes(const Geo& g, int c, int kind, int64_t rows, int64_t cols,
-                       NsBuffers* b, float** partials, float** xscale, void* base,
+                       NsBuffers* b, double** partials, float** xscale, void* base,
                        size_t gemm_cap = kGemmScratchBytes) {
   Carver cv(base);
   NsBuffers tmp;
   NsBuffers& nb = b ? *b : tmp;
-  float* p = cv.take<float>((size_t)c * norm_blocks(rows * cols));
+  double* p = cv.take<double>((size_t)c * norm_blocks(rows * cols));
   float* x = cv.take<float>((size_t)c);
   carve_ns(cv, g, c, kind, nb, gemm_cap);
   if (partials) *partials = p;
@@ -689,7 +689,8 @@ static mns_status run_orthogonalize(const void* X, void* O, Store sto, const Geo
   for (int64_t b0 = 0; b0 < batch; b0 += cmax) {
     const int c = (int)((batch - b0) < cmax ? batch - b0 : cmax);
     NsBuffers nb;
-    float *partials = nullptr, *xscale = nullptr;
+    double* partials = nullptr;
+    float* xscale = nullptr;
     ns_bytes(g, c, kind, rows, cols, &nb, &partials, &xscale, ws, gemm_cap);
     const bool km = kmajor_ns(g, c, nb);
     const char* xin = static_cast<const char*>(X) + (size_t)b0 * rows * cols * esz;

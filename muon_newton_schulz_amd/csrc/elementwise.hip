@@ -167,17 +167,25 @@ __device__ __forceinline__ T block_sum(T v, T* sh) {
   return r;
 }
 
+// Sum of the squares of four float32 values, squared and added in float64.
+__device__ __forceinline__ double sq4(const float4& v) {
+  const double x = v.x, y = v.y, z = v.z, w = v.w;
+  return x * x + y * y + z * z + w * w;
+}
+
 // ---- a1: momentum M <- mu M + G, partial sums of M^2 (Eq. 1) --------------------------------
+// The squares are summed in float64: ||M||_F stays exact in range for any float32 M (squares
+// of |M| < 1e-19 underflow in float32, of |M| > 2e19 overflow), and the method is scale-free.
 
 template <typename TG>
 __global__ __launch_bounds__(kThreads) void k_momentum(PtrPack Mp, PtrPack Gp, int64_t elems,
-                                                       float mu, float* partials, int nblk) {
-  __shared__ float sh[kThreads / 64];
+                                                       float mu, double* partials, int nblk) {
+  __shared__ double sh[kThreads / 64];
   const int b = blockIdx.y;
   float* m = static_cast<float*>(Mp.p[b]);
   const TG* g = static_cast<const TG*>(Gp.p[b]);
   const int64_t nvec = elems / 4;
-  float acc = 0.f;
+  double acc = 0.0;
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     const int64_t v = ((int64_t)blockIdx.x * kIter + it) * kThreads + threadIdx.x;
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void k_momentum(PtrPack Mp, PtrPack Gp, i
       mv.z = fmaf(mu, mv.z, gv.z);
       mv.w = fmaf(mu, mv.w, gv.w);
       store4<float>(m, 4 * v, mv);
-      acc += mv.x * mv.x + mv.y * mv.y + mv.z * mv.z + mv.w * mv.w;
+      acc += sq4(mv);
     }
   }
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x < 4) {
@@ -197,50 +205,50 @@ __global__ __launch_bounds__(kThreads) void k_momentum(PtrPack Mp, PtrPack Gp, i
     if (e < elems) {
       const float mv = fmaf(mu, m[e], load1<TG>(g, e));
       m[e] = mv;
-      acc += mv * mv;
+      acc += (double)mv * (double)mv;
     }
   }
-  const float s = block_sum<float, kThreads>(acc, sh);
+  const double s = block_sum<double, kThreads>(acc, sh);
   if (threadIdx.x == 0) partials[(int64_t)b * nblk + blockIdx.x] = s;
 }
 
 // ---- partial sums of X^2 for a stored matrix (X / ||X||_F of standard NS) ------------------
 
 template <typename TX>
-__global__ __launch_bounds__(kThreads) void k_sumsq(const TX* X, int64_t elems, float* partials,
+__global__ __launch_bounds__(kThreads) void k_sumsq(const TX* X, int64_t elems, double* partials,
                                                     int nblk) {
-  __shared__ float sh[kThreads / 64];
+  __shared__ double sh[kThreads / 64];
   const int b = blockIdx.y;
   const TX* x = X + (int64_t)b * elems;
   const int64_t nvec = elems / 4;
-  float acc = 0.f;
+  double acc = 0.0;
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     const int64_t v = ((int64_t)blockIdx.x * kIter + it) * kThreads + threadIdx.x;
     if (v < nvec) {
       const float4 xv = load4<TX>(x, 4 * v);
-      acc += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+      acc += sq4(xv);
     }
   }
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x < 4) {
     const int64_t e = nvec * 4 + threadIdx.x;
     if (e < elems) {
       const float xv = load1<TX>(x, e);
-      acc += xv * xv;
+      acc += (double)xv * (double)xv;
     }
   }
-  const float s = block_sum<float, kThreads>(acc, sh);
+  const double s = block_sum<double, kThreads>(acc, sh);
   if (threadIdx.x == 0) partials[(int64_t)b * nblk + blockIdx.x] = s;
 }
 
 // ---- a2: 1/||M||_F (times the iterate's storage scale) ----------------------------------------
 
-__global__ __launch_bounds__(kThreads) void k_finalize_scale(const float* partials, int nblk,
+__global__ __launch_bounds__(kThreads) void k_finalize_scale(const double* partials, int nblk,
                                                              float S, float* xscale) {
   __shared__ double sh[kThreads / 64];
   const int b = blockIdx.x;
   double acc = 0.0;
-  for (int i = threadIdx.x; i < nblk; i += kThreads) acc += (double)partials[(int64_t)b * nblk + i];
+  for (int i = threadIdx.x; i < nblk; i += kThreads) acc += partials[(int64_t)b * nblk + i];
   const double s = block_sum<double, kThreads>(acc, sh);
   if (threadIdx.x == 0) xscale[b] = s > 0.0 ? (float)((double)S / sqrt(s)) : 0.f;
 }
@@ -628,14 +636,16 @@ __global__ __launch_bounds__(kThreads) void k_rowscale_apply(TO* O, int64_t rows
 
 template <typename TG>
 __global__ __launch_bounds__(kThreads) void k_momentum_l1(PtrPack Mp, PtrPack Gp, int64_t rows,
-                                                          int64_t cols, float* l1, float* l2sq) {
+                                                          int64_t cols, float* l1, double* l2sq) {
   __shared__ float sh[kThreads / 64];
+  __shared__ double dsh[kThreads / 64];
   const int b = blockIdx.y;
   float* m = static_cast<float*>(Mp.p[b]);
   const TG* g = static_cast<const TG*>(Gp.p[b]);
   const bool vec_ok = (cols % 4) == 0;
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    float acc = 0.f, acc2 = 0.f;
+    float acc = 0.f;
+    double acc2 = 0.0;   // float64 squares, as in k_momentum
     if (vec_ok) {
       for (int64_t j = (int64_t)threadIdx.x * 4; j < cols; j += kThreads * 4) {
         float4 mv = load4<float>(m, r * cols + j);
@@ -643,18 +653,18 @@ __global__ __launch_bounds__(kThreads) void k_momentum_l1(PtrPack Mp, PtrPack Gp
         mv.x += gv.x; mv.y += gv.y; mv.z += gv.z; mv.w += gv.w;
         store4<float>(m, r * cols + j, mv);
         acc += fabsf(mv.x) + fabsf(mv.y) + fabsf(mv.z) + fabsf(mv.w);
-        acc2 += mv.x * mv.x + mv.y * mv.y + mv.z * mv.z + mv.w * mv.w;
+        acc2 += sq4(mv);
       }
     } else {
       for (int64_t j = threadIdx.x; j < cols; j += kThreads) {
         const float mv = m[r * cols + j] + load1<TG>(g, r * cols + j);
         m[r * cols + j] = mv;
         acc += fabsf(mv);
-        acc2 += mv * mv;
+        acc2 += (double)mv * (double)mv;
       }
     }
     const float s = block_sum<float, kThreads>(acc, sh);
-    const float s2 = block_sum<float, kThreads>(acc2, sh);
+    const double s2 = block_sum<double, kThreads>(acc2, dsh);
     if (threadIdx.x == 0) {
       l1[(int64_t)b * rows + r] = s;
       l2sq[(int64_t)b * rows + r] = s2;
@@ -706,7 +716,7 @@ __device__ int block_exclusive_scan(int v, int* sh) {
   return res;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, const float* l2sq,
+__global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, const double* l2sq,
                                                       int64_t rows, int64_t k, int32_t* S,
                                                       float Spow, float* xscale) {
   __shared__ uint32_t hist[kSelWaves][256];
@@ -766,14 +776,14 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, const flo
   int pos = block_exclusive_scan(sel, scan_sh);
   int e = eq_before;
   int32_t* out = S + (int64_t)b * k;
-  const float* sq = l2sq + (int64_t)b * rows;
+  const double* sq = l2sq + (int64_t)b * rows;
   double ssq = 0.0;
   for (int64_t i = i0; i < i1; ++i) {
     const uint32_t u = order_key(key[i]);
     const bool take = u > prefix || (u == prefix && e++ < remaining);
     if (take) {
       out[pos++] = (int32_t)i;
-      ssq += (double)sq[i];
+      ssq += sq[i];
     }
   }
   // ||M[S,:]||_F from the selected rows' sums of squares (fixed order): the normalisation
@@ -800,7 +810,7 @@ int norm_blocks(int64_t elems) {
 }
 
 hipError_t momentum(const PtrPack& M, const PtrPack& G, Store g_store, int count, int64_t elems,
-                    float mu, float* partials, hipStream_t s) {
+                    float mu, double* partials, hipStream_t s) {
   const int nblk = norm_blocks(elems);
   dim3 grid(nblk, count);
   if (g_store == Store::BF16)
@@ -810,7 +820,7 @@ hipError_t momentum(const PtrPack& M, const PtrPack& G, Store g_store, int count
   return last();
 }
 
-hipError_t sumsq(const void* X, Store st, int count, int64_t elems, float* partials, hipStream_t s) {
+hipError_t sumsq(const void* X, Store st, int count, int64_t elems, double* partials, hipStream_t s) {
   const int nblk = norm_blocks(elems);
   dim3 grid(nblk, count);
   if (st == Store::BF16)
@@ -822,7 +832,7 @@ hipError_t sumsq(const void* X, Store st, int count, int64_t elems, float* parti
   return last();
 }
 
-hipError_t finalize_scale(const float* partials, int nblk, int count, float S, float* xscale,
+hipError_t finalize_scale(const double* partials, int nblk, int count, float S, float* xscale,
                           hipStream_t s) {
   hipLaunchKernelGGL(k_finalize_scale, dim3(count), dim3(kThreads), 0, s, partials, nblk, S, xscale);
   return last();
@@ -968,7 +978,7 @@ hipError_t rowscale_apply(void* O, Store st, int count, int64_t rows, int64_t co
 }
 
 hipError_t momentum_l1(const PtrPack& M, const PtrPack& G, Store g_store, int count, int64_t rows,
-                       int64_t cols, float* l1, float* l2sq, hipStream_t s) {
+                       int64_t cols, float* l1, double* l2sq, hipStream_t s) {
   dim3 grid(grid_rows(rows), count);
   if (g_store == Store::BF16)
     hipLaunchKernelGGL(k_momentum_l1<uint16_t>, grid, dim3(kThreads), 0, s, M, G, rows, cols, l1, l2sq);
@@ -977,7 +987,7 @@ hipError_t momentum_l1(const PtrPack& M, const PtrPack& G, Store g_store, int co
   return last();
 }
 
-hipError_t topk_rows(const float* l1, const float* l2sq, int count, int64_t rows, int64_t k,
+hipError_t topk_rows(const float* l1, const double* l2sq, int count, int64_t rows, int64_t k,
                      float Spow, int32_t* S, float* xscale, hipStream_t s) {
   hipLaunchKernelGGL(k_topk, dim3(count), dim3(kSelThreads), 0, s, l1, l2sq, rows, k, S, Spow,
                      xscale);

@@ -89,16 +89,16 @@ bool gemm_kmajor_ok(const GemmDesc& d);
 int norm_blocks(int64_t elems);
 
 // M <- mu M + G over `count` same-size matrices; partials[b * nblk + blk] = partial sum of
-// the new M^2.
+// the new M^2 (squares summed in float64: no underflow or overflow for any float32 M).
 hipError_t momentum(const PtrPack& M, const PtrPack& G, Store g_store, int count,
-                    int64_t elems, float mu, float* partials, hipStream_t s);
+                    int64_t elems, float mu, double* partials, hipStream_t s);
 
-// partials of sum X^2 for X of storage type `st` (X_b = X + b * elems).
-hipError_t sumsq(const void* X, Store st, int count, int64_t elems, float* partials,
+// partials of sum X^2 for X of storage type `st` (X_b = X + b * elems), float64.
+hipError_t sumsq(const void* X, Store st, int count, int64_t elems, double* partials,
                  hipStream_t s);
 
 // xscale[b] = S / sqrt(sum_blk partials[b * nblk + blk]), 0 for a zero matrix.
-hipError_t finalize_scale(const float* partials, int nblk, int count, float S, float* xscale,
+hipError_t finalize_scale(const double* partials, int nblk, int count, float S, float* xscale,
                           hipStream_t s);
 
 // The normalised iterate in both layouts, zero padded: S (rows_p x cols_p, pitch
@@ -155,10 +155,10 @@ hipError_t rowscale_apply(void* O, Store st, int count, int64_t rows, int64_t co
 
 // Dion3 (Algorithm 4): M <- M + G with per-row l1 norms and sums of squares of the new M.
 hipError_t momentum_l1(const PtrPack& M, const PtrPack& G, Store g_store, int count,
-                       int64_t rows, int64_t cols, float* l1, float* l2sq, hipStream_t s);
+                       int64_t rows, int64_t cols, float* l1, double* l2sq, hipStream_t s);
 // S[b][rank] = row for the k rows of largest l1 (ties: lower index first), and
 // xscale[b] = Spow / ||M[S,:]||_F from the selected rows' sums of squares (0 for a zero block).
-hipError_t topk_rows(const float* l1, const float* l2sq, int count, int64_t rows, int64_t k,
+hipError_t topk_rows(const float* l1, const double* l2sq, int count, int64_t rows, int64_t k,
                      float Spow, int32_t* S, float* xscale, hipStream_t s);
 // The normalised iterate of the selected rows, like normalize() with row r of the source
 // being M[S[r]] (float32), and in the same pass M[S[r]][:] *= mu.

@@ -302,3 +302,32 @@ def test_zero_matrices_among_others(kind, f):
         check_weight(to_f64(W[i]), W_before[i], ref["W_exact"] - W_before[i], "bf16", f"W[{i}]")
         assert rel(to_f64(M[i]), ref["M"]) < 1e-6, f"M[{i}]"
         assert rel(to_f64(v[i]), ref["v"]) < TOL["bf16"], f"v[{i}]"
+
+
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [1e-24, 1e24])
+def test_extreme_scales(storage, scale):
+    """The orthogonalisation is scale-free (X_0 = M / ||M||_F): momenta and gradients whose
+    squares underflow (1e-24) or overflow (1e24) float32 give the same step as the oracle's,
+    through the step (k_momentum's norm) and the standalone entry point (k_sumsq's)."""
+    _say("case extreme scale", storage, scale)
+    r, c, mu, lr = 300, 700, 0.9, 0.05
+    W = to_device(synthetic.weight(r, c, storage, 970, 0), storage)
+    M0 = synthetic.state(r, c, 970, 0, scale=0.5).astype(np.float64) * scale
+    g = synthetic.gradient("student_t", r, c, "f32", 971, 0, 0).astype(np.float64) * scale
+    G = (torch.from_numpy(g.astype(np.float32)).cuda() if storage == "f32"
+         else torch.from_numpy(g.astype(np.float32)).cuda().to(torch.bfloat16))
+    M = torch.from_numpy(M0.astype(np.float32)).cuda()
+    W_before, M_before, g64 = to_f64(W), to_f64(M), to_f64(G)
+    mns.muon_step([W], [M], [G], None, mu=mu, lr=lr, coeffs=[QUINTIC] * 5)
+    torch.cuda.synchronize()
+    ref = oracle.muon_step(W_before, M_before, g64, mu=mu, lr=lr, coeffs=[QUINTIC] * 5,
+                           storage=storage)
+    check_weight(to_f64(W), W_before, ref["W_exact"] - W_before, storage, "W")
+    assert rel(to_f64(M), ref["M"]) < 1e-6
+    # the standalone orthogonalisation of the gradient itself
+    O = mns.ns_orthogonalize(G, [QUINTIC] * 5)
+    torch.cuda.synchronize()
+    O_ref = oracle.newton_schulz(g64, [QUINTIC] * 5)
+    assert torch.isfinite(O.float()).all()
+    assert rel(to_f64(O), O_ref) < TOL[storage]
