@@ -18,6 +18,10 @@ default workload is the largest: the 196-matrix layer set of a 3B-like transform
   * gram_ns_same_matrices: the step with Gram Newton-Schulz (restart before iteration 3) on
     the same resident matrices, and its speedup over the standard-NS step;
   * gpu_clocks: the graphics and memory clocks (and socket power) read during the timed steps;
+  * mfma_ceiling: the rate of an MFMA-only kernel (no memory traffic) with random and with
+    zero float16 operands on this part, right after the timed work: what the matrix pipes
+    sustain at the clock the power limit leaves them; the roofline and the gate are also
+    given as fractions of it (beside the published peak, which stays their `peak`);
   * cpu_baseline: the fp64 oracle on a bounded sample, on the host's cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {1..7}] [--kind standard|gram]
@@ -65,6 +69,8 @@ def parse(argv=None):
                     help="skip the cache-flushed timing of the HBM kernels")
     ap.add_argument("--no-gram", action="store_true",
                     help="skip the Gram NS timing on the same matrices")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the MFMA-only ceiling probe and print its JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args(argv)
@@ -310,6 +316,7 @@ class ClockSampler:
     def __init__(self):
         self.h = None
         self.sys, self.mem, self.power = [], [], []
+        self.t0 = self.t1 = None
         try:
             amdsmi = self._amdsmi()
             hs = amdsmi.amdsmi_get_processor_handles()
@@ -321,6 +328,9 @@ class ClockSampler:
     def sample(self):
         if self.h is None:
             return
+        now = time.perf_counter()
+        self.t0 = now if self.t0 is None else self.t0
+        self.t1 = now
         a = self.amdsmi
         try:
             self.sys.append(a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.SYS)["clk"])
@@ -339,14 +349,49 @@ class ClockSampler:
         def stats(v):
             v = [x for x in v if isinstance(x, (int, float))]
             return {"mean": round(sum(v) / len(v), 1), "min": min(v), "max": max(v)} if v else None
+        # amdsmi refreshes these readings about once a second: a window much shorter than that
+        # can show the values from before the work started
+        window = round(self.t1 - self.t0, 3) if self.t0 is not None else None
         out = {"sys_clock_mhz": stats(self.sys), "mem_clock_mhz": stats(self.mem),
                "socket_power_w": stats(self.power), "samples": len(self.sys),
+               "window_s": window, "reliable": window is not None and window >= 1.0,
                "source": "amdsmi" if self.h is not None else None}
         # context: the published dense peak assumes 2.4 GHz; the peak at the clock held here
         if out["sys_clock_mhz"]:
             out["f16_peak_tflops_at_mean_clock"] = round(
                 PEAK_TFLOPS["f16"] * out["sys_clock_mhz"]["mean"] / PEAK_CLOCK_MHZ, 1)
         return out
+
+
+def mfma_ceiling(torch, iters=30000, reps=24):
+    """The MFMA-only probe (libmns_probe.so): `reps` launches of about 40 ms each with random
+    float16 operands, then with zero operands; each rate is the median of the second half of
+    its launches (after the clock has settled). The clock each ran at comes from counters
+    (GRBM_GUI_ACTIVE under rocprofv3): amdsmi's readings trail a change of load by most of a
+    second."""
+    from muon_newton_schulz_amd import probe
+    stream = torch.cuda.current_stream()
+    out = {"kernel": "v_mfma_f32_32x32x16_f16 only, 4 independent accumulators per wave, "
+                     "8 workgroups of 4 waves per CU, no memory traffic in the loop",
+           "iters": iters, "launches": reps}
+    for zero in (False, True):
+        times, flops = [], 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            flops = probe.mfma_launch(iters, zero, stream)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        settled = sorted(times[reps // 2:])
+        ms = settled[len(settled) // 2]
+        check = probe.mfma_checksum(4096)
+        key = "zero_operands" if zero else "random_operands"
+        out[key] = {"tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["f16"], 4),
+                    "ms_per_launch": round(ms, 3), "checksum": check}
+    out["tflops"] = out["random_operands"]["tflops"]
+    return out
 
 
 class Workload:
@@ -409,6 +454,10 @@ def main(argv=None):
     args = parse(argv)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.mfma_ceiling:
+        import torch
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(torch)}), flush=True)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -543,6 +592,15 @@ def main(argv=None):
         del gw
         torch.cuda.empty_cache()
 
+    # What the matrix pipes sustain on this part right now (random operands), for reading the
+    # fractions of the published peak above.
+    say("MFMA-only ceiling")
+    ceiling = mfma_ceiling(torch)
+    if roof["bound"] == "mfma" and dtype == "f16":
+        roof["frac_of_sustained_mfma"] = round(roof["achieved"] / ceiling["tflops"], 4)
+    if gate is not None:
+        gate["ns_gemm_frac_of_sustained_mfma"] = round(gate["ns_gemm_tflops"] / ceiling["tflops"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         say("oracle sample on the host")
@@ -573,6 +631,7 @@ def main(argv=None):
         "mfma_frac_step": round(value / peak, 4),
         "roofline": roof,
         "gpu_clocks": clocks.summary(),
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "ns_gate_4096x16384": gate,
         "gram_ns_same_matrices": gram,

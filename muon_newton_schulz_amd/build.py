@@ -1,4 +1,6 @@
-"""Build the HIP library (gfx950) in-tree: muon_newton_schulz_amd/libmuon_ns.so.
+"""Build the HIP libraries (gfx950) in-tree: muon_newton_schulz_amd/libmuon_ns.so (the
+optimizer step) and muon_newton_schulz_amd/libmns_probe.so (the MFMA ceiling probe, a
+measurement aid).
 
 Usage: python -m muon_newton_schulz_amd.build [--verbose]
 """
@@ -18,6 +20,9 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "elementwise.hip", "gemm.hip"]
+PROBE_NAME = "libmns_probe.so"
+PROBE_PATH = os.path.join(PKG, PROBE_NAME)
+PROBE_SOURCES = ["probe.hip"]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -34,13 +39,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every source for gfx950 and link the shared library. Returns its path."""
-    cc = hipcc()
+def _compile_link(cc, sources, out_path, verbose, extra_flags):
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
-    for src in SOURCES:
+    for src in sources:
         path = os.path.join(CSRC, src)
         obj = os.path.join(objdir, src + ".o")
         cmd = [cc, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC,
@@ -54,12 +57,20 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         if verbose and noise:
             print("\n".join(noise))
         objs.append(obj)
-    tmp = LIB_PATH + ".tmp"
+    tmp = out_path + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out_path)
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+    """Compile every source for gfx950 and link both shared libraries. Returns the path of
+    the optimizer-step library."""
+    cc = hipcc()
+    _compile_link(cc, SOURCES, LIB_PATH, verbose, extra_flags)
+    _compile_link(cc, PROBE_SOURCES, PROBE_PATH, verbose, extra_flags)
     return LIB_PATH
 
 

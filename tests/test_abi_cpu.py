@@ -26,6 +26,43 @@ def _declared_functions():
     return sorted(set(n for n in names if n not in ("defined",)))
 
 
+PROBE_HEADER = os.path.join(ROOT, "include", "mns_probe.h")
+
+
+def _declared_in(header):
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_every_header_is_covered():
+    # each header under include/ has its library and its list of exports checked here
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["mns_probe.h", "muon_ns.h"]
+
+
+def test_probe_header_declares_its_exports_and_the_library_exports_them():
+    from muon_newton_schulz_amd import probe
+    assert sorted(probe.EXPORTS) == _declared_in(PROBE_HEADER)
+    lib = probe.load()
+    for name in probe.EXPORTS:
+        assert hasattr(lib, name), name
+
+
+def test_probe_rejects_bad_arguments_before_any_hip_call():
+    import ctypes
+    from muon_newton_schulz_amd import probe
+    lib = probe.load()
+    f = ctypes.c_double(0.0)
+    assert lib.mns_probe_mfma_launch(0, 0, None, ctypes.byref(f)) == 4
+    assert lib.mns_probe_mfma_launch(1000001, 0, None, ctypes.byref(f)) == 4
+    assert lib.mns_probe_mfma_launch(10, 0, None, None) == 4
+    assert lib.mns_probe_mfma_checksum(0, ctypes.byref(f)) == 4
+    assert lib.mns_probe_mfma_checksum(10, None) == 4
+    # nothing launched yet in this process: no results to read
+    assert lib.mns_probe_mfma_checksum(10, ctypes.byref(f)) == 4
+
+
 def test_header_declares_the_exports():
     assert sorted(_abi.EXPORTS) == _declared_functions()
 

@@ -81,4 +81,5 @@ def test_clock_sampler_reports_fields_without_a_device():
     c = bench.ClockSampler()
     c.sample()
     s = c.summary()
-    assert set(s) == {"sys_clock_mhz", "mem_clock_mhz", "socket_power_w", "samples", "source"}
+    assert set(s) == {"sys_clock_mhz", "mem_clock_mhz", "socket_power_w", "samples", "window_s",
+                      "reliable", "source"}

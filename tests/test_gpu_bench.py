@@ -64,3 +64,10 @@ def test_bench_line_with_gate_and_gram():
     assert "sys_clock_mhz" in d["gpu_clocks"]
     flushed = d["hbm_kernels_cache_flushed"]["kernels"]
     assert "momentum" in flushed and 0 < flushed["momentum"]["frac"] < 1
+    # the MFMA-only ceiling: below the published peak's reach, above what the GEMMs achieve
+    # per launch, and the fractions of it consistent with the rates they divide
+    ceil = d["mfma_ceiling"]
+    assert 0 < ceil["tflops"] <= 1.05 * 2500.0
+    assert ceil["zero_operands"]["checksum"] == 0.0
+    assert abs(d["roofline"]["frac_of_sustained_mfma"] - d["roofline"]["achieved"] / ceil["tflops"]) < 1e-3
+    assert abs(gate["ns_gemm_frac_of_sustained_mfma"] - gate["ns_gemm_tflops"] / ceil["tflops"]) < 1e-3
