@@ -71,6 +71,8 @@ def parse(argv=None):
                     help="skip the Gram NS timing on the same matrices")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the MFMA-only ceiling probe and print its JSON")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the MFMA-only ceiling probe (kernel traces of the step alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args(argv)
@@ -594,12 +596,14 @@ def main(argv=None):
 
     # What the matrix pipes sustain on this part right now (random operands), for reading the
     # fractions of the published peak above.
-    say("MFMA-only ceiling")
-    ceiling = mfma_ceiling(torch)
-    if roof["bound"] == "mfma" and dtype == "f16":
-        roof["frac_of_sustained_mfma"] = round(roof["achieved"] / ceiling["tflops"], 4)
-    if gate is not None:
-        gate["ns_gemm_frac_of_sustained_mfma"] = round(gate["ns_gemm_tflops"] / ceiling["tflops"], 4)
+    ceiling = None
+    if not args.no_mfma_ceiling:
+        say("MFMA-only ceiling")
+        ceiling = mfma_ceiling(torch)
+        if roof["bound"] == "mfma" and dtype == "f16":
+            roof["frac_of_sustained_mfma"] = round(roof["achieved"] / ceiling["tflops"], 4)
+        if gate is not None:
+            gate["ns_gemm_frac_of_sustained_mfma"] = round(gate["ns_gemm_tflops"] / ceiling["tflops"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
