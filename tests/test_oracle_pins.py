@@ -343,6 +343,20 @@ def test_select_rows_ties_prefer_lower_index():
     assert oracle.select_rows(M, 4).tolist() == [4, 1, 2, 3]
 
 
+def test_select_rows_nonfinite_norms():
+    """Non-finite norms (a reading of Algorithm 4, which is silent on them): an infinite l1 norm
+    ranks above every finite one, a NaN norm below every number, and equal keys, NaN ones
+    included, go to the lower row index."""
+    M = np.ones((6, 4))
+    M[1, 2] = np.nan
+    M[4, 0] = np.nan
+    M[3, 1] = np.inf
+    M[5] *= 2.0
+    # l1: 4, NaN, 4, inf, NaN, 8
+    assert oracle.select_rows(M, 6).tolist() == [3, 5, 0, 2, 1, 4]
+    assert oracle.select_rows(M, 4).tolist() == [3, 5, 0, 2]
+
+
 def test_rows_for_fraction():
     assert oracle.rows_for_fraction(0.25, 5120) == 1280
     assert oracle.rows_for_fraction(1 / 3, 10) == 4
