@@ -1,5 +1,6 @@
-"""A seeded sweep of ragged shapes and batch sizes through both Newton-Schulz entry points and
-through one grouped step, in both storages, against the fp64 oracle: sizes on either side of
+"""A seeded sweep of ragged shapes and batch sizes through both Newton-Schulz entry points,
+through one grouped step and through Dion3 steps at several row fractions, against the fp64
+oracle: sizes on either side of
 the 64-, 128- and 256-element tile and padding boundaries, below one tile and just past one,
 wide and tall, single and batched. The cases come from a fixed generator (the same on every
 run). Tolerances as elsewhere: relative Frobenius 2e-2 (bfloat16 storage), 1e-4 (float32)."""
@@ -81,3 +82,45 @@ def test_grouped_step_sweep(storage):
         check_weight(to_f64(W[i]), w64, ref["W_exact"] - w64, storage, f"W[{i}] {shapes[i]}")
         assert rel(to_f64(M[i]), ref["M"]) < 1e-6, f"M[{i}]"
         assert rel(to_f64(v[i]), ref["v"]) < TOL[storage], f"v[{i}]"
+
+
+def _dion3_cases(n=6, seed=2027):
+    rng = np.random.default_rng(seed)
+    fracs = [0.125, 0.25, 1.0 / 3, 0.5, 0.9]
+    out = []
+    for i in range(n):
+        r, c = (int(x) for x in rng.choice(EDGES[2:], size=2))   # at least 63 rows
+        out.append((f"{i:02d}", r, c, float(rng.choice(fracs)), ("gram", "standard")[i % 2]))
+    return out
+
+
+DION3_CASES = _dion3_cases()
+
+
+@pytest.mark.parametrize("case", DION3_CASES,
+                         ids=[f"{c[0]}_{c[1]}x{c[2]}_f{c[3]:.3f}_{c[4]}" for c in DION3_CASES])
+def test_dion3_sweep(case):
+    """Dion3 steps (NorMuon on the selected rows) over the sweep's shapes and several row
+    fractions, with Gram and with standard NS, against the oracle's step from the same state
+    (the oracle's own selection: random data leaves no near ties at the k-th row)."""
+    idx, r, c, f, kind = case
+    _say("dion3", idx, (r, c), f, kind)
+    mu, lr = 0.9, 0.05
+    restarts = (3,) if kind == "gram" else ()
+    W0 = synthetic.weight(r, c, "bf16", 995, int(idx))
+    M0 = synthetic.state(r, c, 996, int(idx), scale=0.5)
+    v0 = np.abs(synthetic.state(r, 1, 997, int(idx), scale=0.01)).reshape(r).astype(np.float32)
+    G = synthetic.gradient("student_t", r, c, "bf16", 998, 0, int(idx))
+    W = to_device(W0, "bf16")
+    M = torch.from_numpy(M0).cuda()
+    v = torch.from_numpy(v0).cuda()
+    mns.muon_step(W, M, to_device(G, "bf16"), v, mu=mu, lr=lr, coeffs=[QUINTIC] * 5, kind=kind,
+                  restart_before=restarts, normuon=True, beta2=0.9, eps=1e-8, row_fraction=f)
+    torch.cuda.synchronize()
+    w64 = stored_f64(W0, "bf16")
+    ref = oracle.dion3_step(w64, M0.astype(np.float64), stored_f64(G, "bf16"), mu=mu, lr=lr, f=f,
+                            coeffs=[QUINTIC] * 5, kind=kind, restart_before=restarts, normuon=True,
+                            v=v0.astype(np.float64), beta2=0.9, eps=1e-8, storage="bf16")
+    check_weight(to_f64(W), w64, ref["W_exact"] - w64, "bf16", "W")
+    assert rel(to_f64(M), ref["M"]) < 1e-6, "M"
+    assert rel(to_f64(v), ref["v"]) < TOL["bf16"], "v"
