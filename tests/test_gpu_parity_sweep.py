@@ -1,9 +1,9 @@
 """A seeded sweep of ragged shapes and batch sizes through both Newton-Schulz entry points,
 through one grouped step and through Dion3 steps at several row fractions, against the fp64
-oracle: sizes on either side of
-the 64-, 128- and 256-element tile and padding boundaries, below one tile and just past one,
-wide and tall, single and batched. The cases come from a fixed generator (the same on every
-run). Tolerances as elsewhere: relative Frobenius 2e-2 (bfloat16 storage), 1e-4 (float32)."""
+oracle: sizes on either side of the 64-, 128- and 256-element tile and padding boundaries,
+below one tile and just past one, wide and tall, single and batched. The cases come from a
+fixed generator (the same on every run). Tolerances as elsewhere: relative Frobenius 2e-2
+(bfloat16 storage), 1e-4 (float32)."""
 import numpy as np
 import pytest
 import torch
