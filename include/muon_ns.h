@@ -24,7 +24,8 @@
  *     matching *_workspace_size call returns. The library allocates no device memory,
  *     keeps no state between calls (apart from an open profiling session, see the end of
  *     this file) and is reentrant; calls on different streams must use different
- *     workspaces.
+ *     workspaces. The one exception is ns_orthogonalize_noalloc: its calls on one GPU
+ *     share a static scratch array and must not overlap.
  *   - Errors: arguments are validated synchronously, before anything is enqueued, and
  *     reported as an mns_status; nothing is enqueued when a call returns an error other
  *     than MNS_ERR_HIP. MNS_ERR_HIP means a kernel launch failed (the stream may hold
