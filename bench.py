@@ -471,6 +471,10 @@ def main(argv=None):
     import numpy as np
     import torch
 
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU: no HIP device is visible", file=sys.stderr)
+        sys.exit(3)
+
     import muon_newton_schulz_amd as mns
     import synthetic
 

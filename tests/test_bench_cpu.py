@@ -1,11 +1,12 @@
-"""Host-side checks of bench.py: the one-GPU guard, input construction and the counter lookup
-(no GPU: inputs are built on the CPU)."""
+"""Host-side checks of bench.py: the one-GPU guard, the message without a GPU, input
+construction and the counter lookup (no GPU: inputs are built on the CPU)."""
 import dataclasses
 import os
 import subprocess
 import sys
 
 import numpy as np
+import pytest
 import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -20,6 +21,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the message a machine without a GPU gets")
+def test_without_a_gpu_bench_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "1"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 3
+    assert "needs a GPU" in r.stderr
 
 
 def test_build_inputs_matches_workload():
