@@ -484,29 +484,41 @@ __global__ __launch_bounds__(kThreads) void k_row_sumsq_stored(const TO* O, int6
 
 // ---- a7: NorMuon (Eq. 2) v update and the per-row step scale --------------------------------
 
-// Stage 1, one thread per row: r_i = inv_s2 * sum over chunks of part, the v update,
-// d_i = 1/(sqrt(v_i) + eps) into rowscale, and per block the float64 sums of r_i and
-// r_i d_i^2 (the squared norms of O and of O-hat) into fin[b][0 / 1][block].
+// Stage 1, 64 rows per block of four waves: r_i = inv_s2 * sum over chunks of part, the v
+// update, d_i = 1/(sqrt(v_i) + eps) into rowscale, and per block the float64 sums of r_i and
+// r_i d_i^2 (the squared norms of O and of O-hat) into fin[b][0 / 1][block]. Wave q sums the
+// chunks c = q (mod 4) of its lane's row in increasing order (the chunks past the last whole
+// group of four go to wave 0), each load 64 consecutive rows of one chunk, and the row sum is
+// (s0 + s1) + (s2 + s3): a fixed order, the same additions as one thread keeping four partial
+// sums.
+constexpr int kRowsPerBlock = 64;
+
 __global__ __launch_bounds__(kThreads) void k_normuon_rows(
     const float* part, int chunks, int64_t rows, int64_t cols, PtrPack vp, float* v_base,
     int64_t v_stride, const int32_t* rowidx, float beta2, float eps, float inv_s2,
     float* rowscale, double* fin) {
+  static_assert(kThreads == 4 * kRowsPerBlock, "four waves of 64 rows");
+  __shared__ float part_sh[4][kRowsPerBlock];
   __shared__ double sh[kThreads / 64];
   const int b = blockIdx.y, nblk = gridDim.x;
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  double s_o = 0.0, s_h = 0.0;
-  if (i < rows) {
-    float* v = v_base ? v_base + (int64_t)b * v_stride : static_cast<float*>(vp.p[b]);
+  const int q = threadIdx.x / kRowsPerBlock, lane = threadIdx.x % kRowsPerBlock;
+  const int64_t i = (int64_t)blockIdx.x * kRowsPerBlock + lane;
+  const bool live = i < rows;
+  float acc = 0.f;
+  if (live) {
     const float* pt = part + (int64_t)b * chunks * rows + i;
-    float r4[4] = {0.f, 0.f, 0.f, 0.f};
-    int c = 0;
-#pragma unroll 4
-    for (; c + 4 <= chunks; c += 4) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) r4[q] += pt[(int64_t)(c + q) * rows];
-    }
-    for (; c < chunks; ++c) r4[0] += pt[(int64_t)c * rows];
-    const float r = ((r4[0] + r4[1]) + (r4[2] + r4[3])) * inv_s2;
+    const int full = chunks - chunks % 4;
+#pragma unroll 8
+    for (int c = q; c < full; c += 4) acc += pt[(int64_t)c * rows];
+    if (q == 0)
+      for (int c = full; c < chunks; ++c) acc += pt[(int64_t)c * rows];
+  }
+  part_sh[q][lane] = acc;
+  __syncthreads();
+  double s_o = 0.0, s_h = 0.0;
+  if (live && q == 0) {
+    float* v = v_base ? v_base + (int64_t)b * v_stride : static_cast<float*>(vp.p[b]);
+    const float r = ((part_sh[0][lane] + part_sh[1][lane]) + (part_sh[2][lane] + part_sh[3][lane])) * inv_s2;
     const int64_t vi = rowidx ? (int64_t)rowidx[(int64_t)b * rows + i] : i;
     const float vn = fmaf(beta2, v[vi], (1.0f - beta2) * (r * (1.0f / (float)cols)));
     v[vi] = vn;
@@ -907,7 +919,7 @@ hipError_t row_sumsq_stored(const void* O, Store st, int count, int64_t rows, in
   return last();
 }
 
-int normuon_blocks(int64_t rows) { return (int)((rows + kThreads - 1) / kThreads); }
+int normuon_blocks(int64_t rows) { return (int)((rows + kRowsPerBlock - 1) / kRowsPerBlock); }
 
 hipError_t normuon_finalize(const float* part, int chunks, int count, int64_t rows, int64_t cols,
                             const PtrPack* v_pack, float* v_base, int64_t v_stride,
