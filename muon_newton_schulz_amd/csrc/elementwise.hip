@@ -728,6 +728,12 @@ __device__ int block_exclusive_scan(int v, int* sh) {
   return res;
 }
 
+// Thread t owns the contiguous rows [t * per, t * per + per) in every pass. When they are at
+// most kSelCache, their keys are read once into registers; otherwise each pass reads them in
+// chunks of kSelCache independent loads. Either way a pass waits for one load latency per
+// chunk instead of one per row, and the counts (so the selection) do not depend on which.
+constexpr int kSelCache = 8;
+
 __global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, const double* l2sq,
                                                       int64_t rows, int64_t k, int32_t* S,
                                                       float Spow, float* xscale) {
@@ -738,15 +744,39 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, const dou
   __shared__ int64_t sh_remaining;
   const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
   const float* key = l1 + (int64_t)b * rows;
+  const int64_t per = (rows + kSelThreads - 1) / kSelThreads;
+  const int64_t i0 = (int64_t)t * per < rows ? (int64_t)t * per : rows;
+  const int64_t i1 = i0 + per < rows ? i0 + per : rows;
+  const bool cached = per <= kSelCache;
+  uint32_t kc[kSelCache];
+#pragma unroll
+  for (int j = 0; j < kSelCache; ++j) kc[j] = (cached && i0 + j < i1) ? order_key(key[i0 + j]) : 0u;
+  // f(row, key) over this thread's rows in ascending row order
+  auto for_keys = [&](auto&& f) {
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < kSelCache; ++j)
+        if (i0 + j < i1) f(i0 + j, kc[j]);
+    } else {
+      for (int64_t c = i0; c < i1; c += kSelCache) {
+        uint32_t u[kSelCache];
+#pragma unroll
+        for (int j = 0; j < kSelCache; ++j) u[j] = c + j < i1 ? order_key(key[c + j]) : 0u;
+#pragma unroll
+        for (int j = 0; j < kSelCache; ++j)
+          if (c + j < i1) f(c + j, u[j]);
+      }
+    }
+  };
+
   uint32_t prefix = 0, mask = 0;
   int64_t remaining = k;   // rows still to take among those whose key matches prefix on mask
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = t; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
     __syncthreads();
-    for (int64_t i = t; i < rows; i += kSelThreads) {
-      const uint32_t u = order_key(key[i]);
+    for_keys([&](int64_t, uint32_t u) {
       if ((u & mask) == prefix) atomicAdd(&hist[wave][(u >> shift) & 255u], 1u);
-    }
+    });
     __syncthreads();
     if (t < 256) {
       uint32_t c = 0;
@@ -771,39 +801,34 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, const dou
     mask |= 255u << shift;
   }
   // keys > K are all taken; of the keys == K, the first `remaining` in index order
-  const int64_t per = (rows + kSelThreads - 1) / kSelThreads;
-  const int64_t i0 = (int64_t)t * per, i1 = i0 + per < rows ? i0 + per : rows;
   int eq = 0;
-  for (int64_t i = i0; i < i1; ++i) eq += order_key(key[i]) == prefix ? 1 : 0;
-  int eq_before = block_exclusive_scan(eq, scan_sh);
+  for_keys([&](int64_t, uint32_t u) { eq += u == prefix ? 1 : 0; });
+  const int eq_before = block_exclusive_scan(eq, scan_sh);
   int sel = 0;
   {
     int e = eq_before;
-    for (int64_t i = i0; i < i1; ++i) {
-      const uint32_t u = order_key(key[i]);
+    for_keys([&](int64_t, uint32_t u) {
       if (u > prefix) ++sel;
       else if (u == prefix) sel += (e++ < remaining) ? 1 : 0;
-    }
+    });
   }
   int pos = block_exclusive_scan(sel, scan_sh);
   int e = eq_before;
   int32_t* out = S + (int64_t)b * k;
   const double* sq = l2sq + (int64_t)b * rows;
   double ssq = 0.0;
-  for (int64_t i = i0; i < i1; ++i) {
-    const uint32_t u = order_key(key[i]);
+  for_keys([&](int64_t i, uint32_t u) {
     const bool take = u > prefix || (u == prefix && e++ < remaining);
     if (take) {
       out[pos++] = (int32_t)i;
       ssq += sq[i];
     }
-  }
+  });
   // ||M[S,:]||_F from the selected rows' sums of squares (fixed order): the normalisation
   // scale of the selected block (0 for a zero block).
   const double tot = block_sum<double, kSelThreads>(ssq, dsh);
   if (t == 0) xscale[b] = tot > 0.0 ? (float)((double)Spow / sqrt(tot)) : 0.f;
 }
-
 
 inline hipError_t last() { return hipGetLastError(); }
 

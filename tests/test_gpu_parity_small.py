@@ -221,6 +221,40 @@ def test_dion3_selection_all_ties():
     assert decayed.tolist() == list(range(75))
 
 
+@pytest.mark.parametrize("rows,pattern", [(9001, "all_ties"), (12004, "pairs")])
+def test_dion3_selection_many_rows(rows, pattern):
+    """More rows than the selection keeps in registers (over 8 per thread of its 1024), so it
+    reads the norms in chunks: the tie order must still follow the row index across the
+    chunks and the threads. "pairs": every l1 norm appears twice, far apart, and k is odd, so
+    one tied pair is split; "all_ties": identical rows, the k of lowest index win."""
+    _say("case dion3 many rows", rows, pattern)
+    cols = 64
+    rng = np.random.default_rng(rows)
+    if pattern == "pairs":
+        # scaled copies of one row, scales 1/rows apart (far above float32's rounding of an
+        # l1 sum), so the float32 and float64 orders agree; each row appears twice
+        v = rng.standard_normal(cols).astype(np.float32)
+        scale = (1.0 + rng.permutation(rows // 2) / rows).astype(np.float32)
+        base = scale[:, None] * v[None, :]
+        G = np.concatenate([base, base[::-1]], axis=0)
+    else:
+        G = np.tile(rng.standard_normal((1, cols)).astype(np.float32), (rows, 1))
+    k = oracle.rows_for_fraction(0.25, rows)
+    assert k % 2 == 1
+    W = torch.zeros(rows, cols, device="cuda")
+    M = torch.zeros(rows, cols, device="cuda")
+    mns.muon_step(W, M, torch.from_numpy(G).cuda(), mu=0.5, lr=0.1, coeffs=[QUINTIC] * 5,
+                  kind="gram", restart_before=(3,), row_fraction=0.25)
+    torch.cuda.synchronize()
+    want = np.sort(oracle.select_rows(G.astype(np.float64), k))
+    if pattern == "all_ties":
+        assert want.tolist() == list(range(k))
+    moved = np.where(W.cpu().numpy().any(axis=1))[0]
+    assert moved.tolist() == want.tolist()
+    decayed = np.where(np.isclose(M.cpu().numpy(), 0.5 * G).all(axis=1))[0]
+    assert decayed.tolist() == want.tolist()
+
+
 @pytest.mark.parametrize("storage", ["bf16", "f32"])
 def test_normuon_scale(storage):
     _say("case normuon", storage)
