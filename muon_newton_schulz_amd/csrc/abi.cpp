@@ -56,6 +56,7 @@ hipError_t timed(const char* name, double flops, double bytes, hipStream_t s, F&
   }
   ProfRec r{name, nullptr, nullptr, flops, bytes};
   if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) {
+    if (r.a) (void)hipEventDestroy(r.a);   // the first event was made, the second was not
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof_failed = true;
     return launch();
