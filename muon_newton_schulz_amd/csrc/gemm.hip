@@ -625,6 +625,13 @@ __global__ __launch_bounds__(256) void k_tail_epilogue(GemmArgs p) {
   // element (ml, nl .. nl+3) of the tile is float4 ((i FN + j) 4 + g) NT + ftid of a part
   const int ml = sm + (threadIdx.x & 63);
   const int wm = ml / WM, i = (ml % WM) / 32, lo = ml % 32;
+  // D for the four pieces first, under one test (not one test per piece).
+  float d[4][4] = {};
+  if (Dg) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      load4<T>(Dg + (int64_t)(m0 + ml) * p.ldd + n0 + sn + 4 * ((threadIdx.x >> 6) + 4 * k), d[k]);
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int nl = sn + 4 * ((threadIdx.x >> 6) + 4 * k);
@@ -632,12 +639,10 @@ __global__ __launch_bounds__(256) void k_tail_epilogue(GemmArgs p) {
     const int64_t idx = ((int64_t)(i * FN + j) * 4 + g) * NT + (wm * WGN + wn) * 64 + hi * 32 + lo;
     floatx4 acc = P[idx];
     for (int part = 1; part < p.fix_parts; ++part) acc += P[(int64_t)part * TILE_F4 + idx];
-    float d[4] = {0.f, 0.f, 0.f, 0.f};
-    if (Dg) load4<T>(Dg + (int64_t)(m0 + ml) * p.ldd + n0 + nl, d);
     t4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float v = p.alpha * acc[e] + p.beta * d[e];
+      float v = p.alpha * acc[e] + p.beta * d[k][e];
       if (m0 + ml == n0 + nl + e && m0 + ml < p.diag_limit) v += p.gamma;
       o[e] = (T)v;
     }
@@ -896,15 +901,21 @@ __global__ __launch_bounds__(256) void k_gemm_kw(GemmArgs p) {
     const T* Dg = p.D ? static_cast<const T*>(p.D) + bz * p.sD : nullptr;
     T* Cg = static_cast<T*>(p.C) + bz * p.sC;
     const bool diag_tile = tm == tn;
+    // D for all four pieces first, under one test: loads placed between the stores below
+    // would each wait for the one before (the stores may alias D as far as the compiler knows).
+    float d[4][4] = {};
+    if (Dg) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        load4<T>(Dg + (int64_t)(m0 + ml) * p.ldd + n0 + wn * 32 + 8 * g + 4 * (lane >> 5), d[g]);
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int nl = wn * 32 + 8 * g + 4 * (lane >> 5);
-      float d[4] = {0.f, 0.f, 0.f, 0.f};
-      if (Dg) load4<T>(Dg + (int64_t)(m0 + ml) * p.ldd + n0 + nl, d);
       t4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float v = p.alpha * acc[0][0][4 * g + e] + p.beta * d[e];
+        float v = p.alpha * acc[0][0][4 * g + e] + p.beta * d[g][e];
         if (m0 + ml == n0 + nl + e && m0 + ml < p.diag_limit) v += p.gamma;
         o[e] = (T)v;
       }
