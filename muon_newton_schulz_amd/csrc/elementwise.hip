@@ -279,31 +279,45 @@ __global__ __launch_bounds__(kThreads) void k_normalize(PtrPack src, const TS* b
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;   // 16 x 8 columns, 16 rows per pass
   const int64_t c = c0 + 8 * tx;
   const bool vec_ok = (cols % 8) == 0;
-  f8 v[kNormRows / 16];
+  // Source offsets, then every load, then the decayed rows (as in k_normalize_rows: a load
+  // after a store to the same array would wait for it).
+  constexpr int NV = kNormRows / 16;
+  const bool full = vec_ok && c + 8 <= cols;
+  f8 v[NV];
+  int64_t soff[NV];
 #pragma unroll
-  for (int i = 0; i < kNormRows / 16; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int64_t r = r0 + ty + 16 * i;
-    v[i] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
-    if (r < rows) {
-      const int64_t sr = GATHER ? (int64_t)rowidx[(int64_t)b * rows + r] : r;
-      if (vec_ok && c + 8 <= cols) {
-        v[i] = load8<TS>(s, sr * cols + c);
-        if constexpr (GATHER) {
-          const f8 w = v[i];
-          store8<float>(const_cast<float*>(s) + sr * cols, c,
-                        {make_float4(mu * w.lo.x, mu * w.lo.y, mu * w.lo.z, mu * w.lo.w),
-                         make_float4(mu * w.hi.x, mu * w.hi.y, mu * w.hi.z, mu * w.hi.w)});
-        }
-      } else {
-        float t8[8];
+    soff[i] = r < rows ? (GATHER ? (int64_t)rowidx[(int64_t)b * rows + r] : r) * cols + c : -1;
+  }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          t8[e] = (c + e < cols) ? load1<TS>(s, sr * cols + c + e) : 0.f;
-          if constexpr (GATHER) {
-            if (c + e < cols) const_cast<float*>(s)[sr * cols + c + e] = mu * t8[e];
-          }
-        }
-        v[i] = {make_float4(t8[0], t8[1], t8[2], t8[3]), make_float4(t8[4], t8[5], t8[6], t8[7])};
+  for (int i = 0; i < NV; ++i) {
+    v[i] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    if (soff[i] < 0) continue;
+    if (full) {
+      v[i] = load8<TS>(s, soff[i]);
+    } else {
+      float t8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t8[e] = (c + e < cols) ? load1<TS>(s, soff[i] + e) : 0.f;
+      v[i] = {make_float4(t8[0], t8[1], t8[2], t8[3]), make_float4(t8[4], t8[5], t8[6], t8[7])};
+    }
+  }
+  if constexpr (GATHER) {
+    // M[S,:] <- mu M[S,:]
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (soff[i] < 0) continue;
+      const f8 w = v[i];
+      if (full) {
+        store8<float>(const_cast<float*>(s), soff[i],
+                      {make_float4(mu * w.lo.x, mu * w.lo.y, mu * w.lo.z, mu * w.lo.w),
+                       make_float4(mu * w.hi.x, mu * w.hi.y, mu * w.hi.z, mu * w.hi.w)});
+      } else {
+        const float t8[8] = {w.lo.x, w.lo.y, w.lo.z, w.lo.w, w.hi.x, w.hi.y, w.hi.z, w.hi.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c + e < cols) const_cast<float*>(s)[soff[i] + e] = mu * t8[e];
       }
     }
   }
@@ -393,37 +407,53 @@ __global__ __launch_bounds__(kThreads) void k_normalize_rows(PtrPack src, const 
   const int64_t nvec = rows_p * vpr;
   const bool vec_ok = (cols % 8) == 0;
   const int64_t v0 = (int64_t)blockIdx.x * kThreads * kRowIter + threadIdx.x;
+  // Source offsets first (with a row index, all of the thread's index loads go out together),
+  // then every load, and only then the decayed rows written back: a load placed after a store
+  // to the same array would wait for that store, one latency per vector.
   f8 v[kRowIter];
-  int64_t dst[kRowIter];
+  int64_t dst[kRowIter], soff[kRowIter];
 #pragma unroll
   for (int it = 0; it < kRowIter; ++it) {
     const int64_t vi = v0 + (int64_t)it * kThreads;
-    v[it] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
     dst[it] = -1;
+    soff[it] = -1;
     if (vi < nvec) {
       const int64_t r = vi / vpr, c = 8 * (vi % vpr);
       dst[it] = r * lds + c;
-      if (r < rows && c < cols) {
-        const int64_t sr = GATHER ? (int64_t)rowidx[(int64_t)b * rows + r] : r;
-        if (vec_ok) {
-          v[it] = load8_nt<TS>(s, sr * cols + c);
-          if constexpr (GATHER) {
-            const f8 w = v[it];
-            store8<float>(const_cast<float*>(s) + sr * cols, c,
-                          {make_float4(mu * w.lo.x, mu * w.lo.y, mu * w.lo.z, mu * w.lo.w),
-                           make_float4(mu * w.hi.x, mu * w.hi.y, mu * w.hi.z, mu * w.hi.w)});
-          }
-        } else {
-          float t8[8];
+      if (r < rows && c < cols)
+        soff[it] = (GATHER ? (int64_t)rowidx[(int64_t)b * rows + r] : r) * cols + c;
+    }
+  }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            t8[e] = (c + e < cols) ? load1<TS>(s, sr * cols + c + e) : 0.f;
-            if constexpr (GATHER) {
-              if (c + e < cols) const_cast<float*>(s)[sr * cols + c + e] = mu * t8[e];
-            }
-          }
-          v[it] = {make_float4(t8[0], t8[1], t8[2], t8[3]), make_float4(t8[4], t8[5], t8[6], t8[7])};
-        }
+  for (int it = 0; it < kRowIter; ++it) {
+    v[it] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    if (soff[it] < 0) continue;
+    if (vec_ok) {
+      v[it] = load8_nt<TS>(s, soff[it]);
+    } else {
+      const int64_t c = 8 * ((v0 + (int64_t)it * kThreads) % vpr);
+      float t8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t8[e] = (c + e < cols) ? load1<TS>(s, soff[it] + e) : 0.f;
+      v[it] = {make_float4(t8[0], t8[1], t8[2], t8[3]), make_float4(t8[4], t8[5], t8[6], t8[7])};
+    }
+  }
+  if constexpr (GATHER) {
+    // M[S,:] <- mu M[S,:] (the selected rows' decay)
+#pragma unroll
+    for (int it = 0; it < kRowIter; ++it) {
+      if (soff[it] < 0) continue;
+      const f8 w = v[it];
+      if (vec_ok) {
+        store8<float>(const_cast<float*>(s), soff[it],
+                      {make_float4(mu * w.lo.x, mu * w.lo.y, mu * w.lo.z, mu * w.lo.w),
+                       make_float4(mu * w.hi.x, mu * w.hi.y, mu * w.hi.z, mu * w.hi.w)});
+      } else {
+        const int64_t c = 8 * ((v0 + (int64_t)it * kThreads) % vpr);
+        const float t8[8] = {w.lo.x, w.lo.y, w.lo.z, w.lo.w, w.hi.x, w.hi.y, w.hi.z, w.hi.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c + e < cols) const_cast<float*>(s)[soff[it] + e] = mu * t8[e];
       }
     }
   }
