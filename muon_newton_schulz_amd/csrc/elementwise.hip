@@ -222,12 +222,20 @@ __global__ __launch_bounds__(kThreads) void k_sumsq(const TX* X, int64_t elems, 
   const TX* x = X + (int64_t)b * elems;
   const int64_t nvec = elems / 4;
   double acc = 0.0;
+  // Every load first, unguarded (a vector past the end re-reads the last one), then the sums
+  // in the same order as before: a load guarded by its own test, with its use in the same
+  // block, made each load wait for the one before.
+  if (nvec > 0) {
+    float4 xv[kIter];
 #pragma unroll
-  for (int it = 0; it < kIter; ++it) {
-    const int64_t v = ((int64_t)blockIdx.x * kIter + it) * kThreads + threadIdx.x;
-    if (v < nvec) {
-      const float4 xv = load4<TX>(x, 4 * v);
-      acc += sq4(xv);
+    for (int it = 0; it < kIter; ++it) {
+      const int64_t v = ((int64_t)blockIdx.x * kIter + it) * kThreads + threadIdx.x;
+      xv[it] = load4<TX>(x, 4 * (v < nvec ? v : nvec - 1));
+    }
+#pragma unroll
+    for (int it = 0; it < kIter; ++it) {
+      const int64_t v = ((int64_t)blockIdx.x * kIter + it) * kThreads + threadIdx.x;
+      if (v < nvec) acc += sq4(xv[it]);
     }
   }
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x < 4) {
@@ -248,6 +256,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize_scale(const double* parti
   __shared__ double sh[kThreads / 64];
   const int b = blockIdx.x;
   double acc = 0.0;
+  // unrolled so several loads are in flight; the additions keep their order
+#pragma unroll 8
   for (int i = threadIdx.x; i < nblk; i += kThreads) acc += partials[(int64_t)b * nblk + i];
   const double s = block_sum<double, kThreads>(acc, sh);
   if (threadIdx.x == 0) xscale[b] = s > 0.0 ? (float)((double)S / sqrt(s)) : 0.f;
@@ -574,6 +584,7 @@ __global__ __launch_bounds__(kThreads) void k_normuon_ratio(const double* fin, i
   __shared__ float scale_sh;
   const int b = blockIdx.x;
   double s_o = 0.0, s_h = 0.0;
+#pragma unroll 4
   for (int k = threadIdx.x; k < nblk; k += kThreads) {
     s_o += fin[((int64_t)b * 2 + 0) * nblk + k];
     s_h += fin[((int64_t)b * 2 + 1) * nblk + k];
@@ -584,6 +595,7 @@ __global__ __launch_bounds__(kThreads) void k_normuon_ratio(const double* fin, i
   __syncthreads();
   const float scale = scale_sh;
   float* rs = rowscale + (int64_t)b * rows;
+#pragma unroll 4
   for (int64_t i = threadIdx.x; i < rows; i += kThreads) rs[i] = rs[i] * scale;
 }
 
