@@ -790,9 +790,20 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, const dou
   const int64_t i0 = (int64_t)t * per < rows ? (int64_t)t * per : rows;
   const int64_t i1 = i0 + per < rows ? i0 + per : rows;
   const bool cached = per <= kSelCache;
+  // The loads are unguarded (an index past the thread's rows is clamped to the last row, and
+  // its key set to 0 after the load): a load guarded by its own test, with its use in the same
+  // block, waited for the one before.
   uint32_t kc[kSelCache];
+  {
+    float kf[kSelCache];
 #pragma unroll
-  for (int j = 0; j < kSelCache; ++j) kc[j] = (cached && i0 + j < i1) ? order_key(key[i0 + j]) : 0u;
+    for (int j = 0; j < kSelCache; ++j) kf[j] = key[i0 + j < rows ? i0 + j : rows - 1];
+#pragma unroll
+    for (int j = 0; j < kSelCache; ++j) {
+      const uint32_t o = order_key(kf[j]);
+      kc[j] = (cached && i0 + j < i1) ? o : 0u;
+    }
+  }
   // f(row, key) over this thread's rows in ascending row order
   auto for_keys = [&](auto&& f) {
     if (cached) {
@@ -801,9 +812,12 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* l1, const dou
         if (i0 + j < i1) f(i0 + j, kc[j]);
     } else {
       for (int64_t c = i0; c < i1; c += kSelCache) {
+        float uf[kSelCache];
         uint32_t u[kSelCache];
 #pragma unroll
-        for (int j = 0; j < kSelCache; ++j) u[j] = c + j < i1 ? order_key(key[c + j]) : 0u;
+        for (int j = 0; j < kSelCache; ++j) uf[j] = key[c + j < i1 ? c + j : i1 - 1];
+#pragma unroll
+        for (int j = 0; j < kSelCache; ++j) u[j] = order_key(uf[j]);
 #pragma unroll
         for (int j = 0; j < kSelCache; ++j)
           if (c + j < i1) f(c + j, u[j]);
