@@ -632,17 +632,32 @@ __global__ __launch_bounds__(256) void k_tail_epilogue(GemmArgs p) {
     for (int k = 0; k < 4; ++k)
       load4<T>(Dg + (int64_t)(m0 + ml) * p.ldd + n0 + sn + 4 * ((threadIdx.x >> 6) + 4 * k), d[k]);
   }
+  // The four pieces' partial sums, part by part: each part's four loads go out together (the
+  // additions per element stay in part order). A part loop inside each piece waited once per
+  // load.
+  int64_t idx[4];
+  floatx4 acc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int nl = sn + 4 * ((threadIdx.x >> 6) + 4 * k);
     const int wn = nl / WN, j = (nl % WN) / 32, g = (nl % 32) / 8, hi = (nl % 8) / 4;
-    const int64_t idx = ((int64_t)(i * FN + j) * 4 + g) * NT + (wm * WGN + wn) * 64 + hi * 32 + lo;
-    floatx4 acc = P[idx];
-    for (int part = 1; part < p.fix_parts; ++part) acc += P[(int64_t)part * TILE_F4 + idx];
+    idx[k] = ((int64_t)(i * FN + j) * 4 + g) * NT + (wm * WGN + wn) * 64 + hi * 32 + lo;
+    acc[k] = P[idx[k]];
+  }
+  for (int part = 1; part < p.fix_parts; ++part) {
+    floatx4 q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = P[(int64_t)part * TILE_F4 + idx[k]];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] += q[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int nl = sn + 4 * ((threadIdx.x >> 6) + 4 * k);
     t4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float v = p.alpha * acc[e] + p.beta * d[k][e];
+      float v = p.alpha * acc[k][e] + p.beta * d[k][e];
       if (m0 + ml == n0 + nl + e && m0 + ml < p.diag_limit) v += p.gamma;
       o[e] = (T)v;
     }
